@@ -1,0 +1,190 @@
+/*
+ * dita.h — C ABI of the partitioned video-DiT attention step with selective
+ * attention-state reuse, native on MI355X (gfx950).
+ *
+ * What the library computes (DiTango, gist.science 2607.15650):
+ *   - the token sequence is split into P contiguous context partitions ("Problematica":
+ *     context parallelism splits the sequence);
+ *   - for query partition i and key partition j the attention state is the pair
+ *       lse_ij[r] = log sum_{c in j} exp(tau q_r . k_c)
+ *       O_ij[r]   = sum_{c in j} exp(tau q_r . k_c - lse_ij[r]) v_c
+ *     ("State-Centric Parallel Runtime / Composizione dello Stato": the cached unit is the
+ *     composed state of output and log-sum-exp, not raw K/V);
+ *   - every block is FRESH (recomputed from this step's Q/K/V and written to its cache
+ *     slot), REUSE (the state its slot holds, written at the step where it was last fresh:
+ *     "Anchor-Guided Selection Planner") or SKIP (outside the active set, e.g.
+ *     Efficient-vDiT's tile-style sparse 3D mask, chatpaper abstract);
+ *   - the states of a row are merged by log-sum-exp, which is associative and commutative:
+ *       L[r] = log sum_j exp(lse_ij[r]);   out[r] = sum_j exp(lse_ij[r] - L[r]) O_ij[r].
+ * tau defaults to 1/sqrt(D) (the pages do not state the scale).
+ *
+ * Conventions
+ *   - Every call returns dita_status; DITA_OK is 0.  Nothing throws or aborts.  On any
+ *     failure no state changes and dita_last_error() returns a thread-local message.
+ *   - Pointers marked "device" are HIP device addresses on the calling thread's current
+ *     device; "host" pointers are ordinary memory.  The library never allocates device
+ *     memory: the caller provides one buffer of dita_cache_required_bytes bytes, which
+ *     holds the state cache, the per-step work lists, a transposed-V scratch and the
+ *     device counters.  The caller owns all device memory and the stream and keeps them
+ *     alive until the stream has passed the step.
+ *   - Q, K, V and out are contiguous [B, H, N, D] (row-major, D fastest).
+ *   - A handle is not thread-safe; different handles are independent.
+ */
+#ifndef DITA_H
+#define DITA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dita_status {
+  DITA_OK = 0,
+  DITA_ERR_INVALID_ARGUMENT = 1, /* null pointer, value out of range                          */
+  DITA_ERR_SHAPE = 2,            /* inconsistent geometry or partition offsets                 */
+  DITA_ERR_UNSUPPORTED = 3,      /* head_dim / dtype combination without a kernel              */
+  DITA_ERR_POLICY = 4,           /* mask value not in {0,1,2}; diagonal not FRESH; a FRESH or
+                                    REUSE block outside the cache's active set                 */
+  DITA_ERR_CACHE_MISS = 5,       /* REUSE of a slot not written since alloc / reset            */
+  DITA_ERR_BUFFER_TOO_SMALL = 6, /* device buffer smaller than dita_cache_required_bytes       */
+  DITA_ERR_NO_POLICY = 7,        /* dita_attn_step without a policy set for this step          */
+  DITA_ERR_DEVICE = 8            /* a HIP call failed (message in dita_last_error)             */
+} dita_status;
+
+typedef enum dita_dtype { DITA_F32 = 0, DITA_BF16 = 1 } dita_dtype;
+
+enum { DITA_SKIP = 0, DITA_FRESH = 1, DITA_REUSE = 2 };
+
+typedef enum dita_policy_kind {
+  DITA_POLICY_EXPLICIT = 0,           /* mask given by the caller                            */
+  DITA_POLICY_FRAME_THRESHOLD = 1,    /* FRESH iff |f_i - f_j| <= max_fresh_frame_dist       */
+  DITA_POLICY_FRESH_BUDGET = 2,       /* per row R = min(floor((pct*A_i + 50)/100), A_i - 1) */
+  DITA_POLICY_CENTROID_THRESHOLD = 3  /* FRESH iff |C_i - C_j| <= max_fresh_centroid2        */
+} dita_policy_kind;
+
+/* Token geometry.  Tokens are (t, y, x) flattened frame-major, row-major inside a frame:
+ * tokens == frames * grid_h * grid_w.  Partition p holds tokens [o_p, o_{p+1}).  Its
+ * doubled centroid is C_p = o_p + o_{p+1} - 1 and its frame is f_p = C_p / (2*grid_h*grid_w)
+ * (integer division): the frame of its centre token. */
+typedef struct dita_geometry {
+  int32_t batch, heads, tokens, head_dim;   /* B, H, N, D.  bf16: D in {64, 72, 128} (72 is
+                                               padded to 96 inside); f32: D <= 64          */
+  int32_t frames, grid_h, grid_w;
+  int32_t num_partitions;                   /* P, 1 <= P <= 1024, P <= N                    */
+  const int32_t* partition_offsets;         /* host, P+1 increasing ints from 0 to N, or
+                                               NULL for the array_split rule (the first
+                                               N mod P partitions get one more token).
+                                               Copied; not kept.                           */
+  dita_dtype qkv_dtype;                     /* element type of Q, K, V                      */
+  dita_dtype cache_o_dtype;                 /* must equal qkv_dtype; cache lse is f32       */
+  float softmax_scale;                      /* tau; <= 0 selects 1/sqrt(D)                  */
+} dita_geometry;
+
+/* One step's block policy (DiTango, "Anchor-Guided Selection Planner"): which blocks are
+ * recomputed and which reuse a cached state.  Candidates for the budget rule are ranked by
+ * (|f_i - f_j|, |C_i - C_j|, j).  Whatever the kind, the diagonal block is FRESH (the local
+ * partition is always computed) and only blocks of the active set are non-SKIP. */
+typedef struct dita_block_policy {
+  int32_t kind;                  /* dita_policy_kind                                         */
+  const uint8_t* explicit_mask;  /* host, P*P row-major, kind == EXPLICIT; copied            */
+  int32_t max_fresh_frame_dist;  /* FRAME_THRESHOLD                                           */
+  int32_t reuse_percent;         /* FRESH_BUDGET, 0..100                                      */
+  int32_t max_fresh_centroid2;   /* CENTROID_THRESHOLD, in doubled-token units                */
+  int32_t tile_sparse;           /* 1: active iff f_j in {f_i, 0, f_i - 1, f_i + 1}
+                                    (Efficient-vDiT's tile-style sparse 3D attention)         */
+  int32_t anchor;                /* 1: every active block FRESH (anchor step)                 */
+} dita_block_policy;
+
+typedef struct dita_step_stats {
+  int64_t steps_done;            /* successful dita_attn_step calls since alloc              */
+  int32_t last_counts[3];        /* SKIP, FRESH, REUSE blocks of the last step (P*P total)   */
+  int32_t reserved;
+  uint64_t device_fresh_blocks;  /* cumulative (b, h, i, j) fresh blocks counted on device   */
+  uint64_t device_reuse_blocks;  /* cumulative (b, h, i, j) reused blocks counted on device  */
+  uint64_t host_fresh_blocks;    /* the same two sums from the host plans, for comparison    */
+  uint64_t host_reuse_blocks;
+  double last_fresh_flops;       /* sum over fresh blocks of 4 n_i n_j D, times B*H          */
+  double last_cache_read_bytes;  /* sum over reused blocks of n_i (D*s_c + 4), times B*H     */
+  double last_cache_write_bytes; /* sum over fresh blocks of n_i (D*s_c + 4), times B*H      */
+} dita_step_stats;
+
+typedef struct dita_cache dita_cache;
+
+/* Library version string (static storage). */
+const char* dita_version(void);
+
+/* Thread-local message describing the last failed call on this thread ("" if none). */
+const char* dita_last_error(void);
+
+/* Evaluate a policy without a cache: host only, integer arithmetic.
+ *   valid     host, P*P, nonzero = the slot holds a state from an earlier step; NULL = none
+ *   mask_out  host, P*P, receives DITA_SKIP / DITA_FRESH / DITA_REUSE
+ * Errors: INVALID_ARGUMENT, SHAPE, POLICY, CACHE_MISS (REUSE where valid is zero). */
+dita_status dita_policy_mask(const dita_geometry* geom, const dita_block_policy* policy,
+                             const uint8_t* valid, uint8_t* mask_out);
+
+/* Partition offsets the geometry resolves to: host out[P+1]. */
+dita_status dita_partition_offsets(const dita_geometry* geom, int32_t* out);
+
+/* Bytes the device buffer must hold for this geometry.
+ *   active_mask  host, P*P, nonzero = the block may ever be FRESH or REUSE (it gets a cache
+ *                slot); NULL = every block. */
+dita_status dita_cache_required_bytes(const dita_geometry* geom, const uint8_t* active_mask,
+                                      size_t* bytes);
+
+/* Create a cache handle bound to a caller-owned device buffer (device, 256-byte aligned,
+ * at least dita_cache_required_bytes).  All slots start invalid, so the first step must be
+ * an anchor (or use no REUSE).  No device work happens here.
+ * Errors: INVALID_ARGUMENT, SHAPE, UNSUPPORTED, BUFFER_TOO_SMALL. */
+dita_status dita_cache_alloc(const dita_geometry* geom, const uint8_t* active_mask,
+                             void* device_buffer, size_t buffer_bytes, dita_cache** out);
+
+/* Invalidate every slot and drop a pending policy; the next step must reuse nothing. */
+dita_status dita_cache_reset(dita_cache* cache);
+
+/* Free the host state; the device buffer stays the caller's.  Waits for steps in flight. */
+dita_status dita_cache_free(dita_cache* cache);
+
+/* Set the policy of the NEXT step.  Validates against the current slot validity.
+ * Errors: INVALID_ARGUMENT, POLICY, CACHE_MISS.  On error the previous pending policy (if
+ * any) is kept. */
+dita_status dita_set_block_policy(dita_cache* cache, const dita_block_policy* policy);
+
+/* The plan of the pending step (or, if none is pending, of the last executed step):
+ *   mask        host P*P
+ *   fresh_ptr   host P+1; fresh_cols host >= counts[1] entries (ascending j per row)
+ *   reuse_ptr   host P+1; reuse_cols host >= counts[2] entries
+ *   counts      host [3]: SKIP, FRESH, REUSE
+ * Any output pointer may be NULL.  Errors: INVALID_ARGUMENT, NO_POLICY. */
+dita_status dita_get_block_plan(const dita_cache* cache, uint8_t* mask, int32_t* fresh_ptr,
+                                int32_t* fresh_cols, int32_t* reuse_ptr, int32_t* reuse_cols,
+                                int32_t* counts);
+
+/* Run one denoising step's attention on `hip_stream` (a hipStream_t; NULL = default).
+ *   q, k, v   device, [B,H,N,D] of qkv_dtype
+ *   out       device, [B,H,N,D] f32: the merged output
+ *   lse_out   device, [B,H,N] f32 natural-log L, or NULL
+ * Fresh blocks are recomputed and written back to their slots; reused blocks are read from
+ * theirs.  Stream-asynchronous: returns after enqueueing.  On success the pending policy is
+ * consumed, written slots become valid and the step counter advances.
+ * Errors: INVALID_ARGUMENT, NO_POLICY, DEVICE. */
+dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, const void* v,
+                           float* out, float* lse_out, void* hip_stream);
+
+/* Copy one cache slot out in plain layout (for checks and export), on `hip_stream`:
+ *   o_out    device, n_i x D f32 row-major: the cached O_ij rows of query partition i
+ *   lse_out  device, n_i f32: the cached lse_ij (natural log)
+ * Errors: INVALID_ARGUMENT (indices), POLICY (block without a slot), CACHE_MISS. */
+dita_status dita_cache_read_slot(dita_cache* cache, int32_t b, int32_t h, int32_t i, int32_t j,
+                                 float* o_out, float* lse_out, void* hip_stream);
+
+/* Counters and last-step work.  Synchronises the device to read the device counters. */
+dita_status dita_get_stats(const dita_cache* cache, dita_step_stats* stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DITA_H */

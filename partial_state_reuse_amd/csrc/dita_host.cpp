@@ -1,0 +1,666 @@
+// Host side of the dita library: geometry, block policy, slot table, work lists,
+// validation, bookkeeping and the C ABI declared in include/dita.h.
+//
+// Method (DiTango, gist.science 2607.15650):
+//   "Anchor-Guided Selection Planner": per step each partition block is recomputed or
+//   reuses a state from an earlier step; anchor steps recompute everything; the local
+//   partition is always computed.
+//   "State-Centric Parallel Runtime / Composizione dello Stato": the cached unit is the
+//   (output, log-sum-exp) state of a block.
+// Efficient-vDiT (chatpaper abstract): tile-style sparse 3D attention (own frame, first
+// frame, neighbouring frames), linear in the number of frames, used as the active set.
+#include "dita.h"
+
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "dita_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dita_status fail(dita_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dita_status ok() { return DITA_OK; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Resolved geometry.
+struct Geo {
+  int B = 0, H = 0, N = 0, D = 0, DP = 0, P = 0;
+  int frames = 0, gh = 0, gw = 0, F = 0;
+  dita_dtype qkv = DITA_BF16, cache_o = DITA_BF16;
+  float tau = 0.f;
+  std::vector<int32_t> offs;    // P+1
+  std::vector<int64_t> c2;      // doubled centroids
+  std::vector<int32_t> frame;   // frame of each partition
+  std::vector<int32_t> poffs;   // P+1 padded offsets (multiples of the key tile)
+  int kt_pad = 0;
+  int wg_rows = 0;
+  int num_tiles = 0;
+  int slot_rows = 0;
+  bool bf16() const { return qkv == DITA_BF16; }
+};
+
+dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
+  if (!g) return fail(DITA_ERR_INVALID_ARGUMENT, "geometry is NULL");
+  Geo r;
+  r.B = g->batch; r.H = g->heads; r.N = g->tokens; r.D = g->head_dim;
+  r.frames = g->frames; r.gh = g->grid_h; r.gw = g->grid_w; r.P = g->num_partitions;
+  if (r.B <= 0 || r.H <= 0 || r.N <= 0 || r.D <= 0)
+    return fail(DITA_ERR_SHAPE, "batch, heads, tokens and head_dim must be positive");
+  if (r.frames <= 0 || r.gh <= 0 || r.gw <= 0)
+    return fail(DITA_ERR_SHAPE, "frames, grid_h and grid_w must be positive");
+  if ((int64_t)r.frames * r.gh * r.gw != r.N)
+    return fail(DITA_ERR_SHAPE, "tokens (%d) != frames*grid_h*grid_w (%lld)", r.N,
+                (long long)r.frames * r.gh * r.gw);
+  if (r.P < 1 || r.P > 1024 || r.P > r.N)
+    return fail(DITA_ERR_SHAPE, "num_partitions must be in 1..min(1024, tokens)");
+  if ((int64_t)r.B * r.H * r.N * r.D >= (int64_t)1 << 40)
+    return fail(DITA_ERR_SHAPE, "tensor too large");
+  r.F = r.gh * r.gw;
+  if (g->qkv_dtype != DITA_F32 && g->qkv_dtype != DITA_BF16)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "unknown qkv_dtype");
+  if (g->cache_o_dtype != g->qkv_dtype)
+    return fail(DITA_ERR_UNSUPPORTED, "cache_o_dtype must equal qkv_dtype");
+  r.qkv = g->qkv_dtype;
+  r.cache_o = g->cache_o_dtype;
+  if (r.bf16()) {
+    r.DP = dita::bf16_padded_dim(r.D);
+    if (!r.DP) return fail(DITA_ERR_UNSUPPORTED, "bf16 head_dim must be a multiple of 8 <= 128");
+    r.wg_rows = dita::bf16_wg_rows(r.DP);
+  } else {
+    if (r.D > 64 || r.D % 4 != 0)
+      return fail(DITA_ERR_UNSUPPORTED, "f32 head_dim must be a multiple of 4 <= 64");
+    r.DP = 64;
+    r.wg_rows = dita::kF32Rows;
+  }
+  r.tau = g->softmax_scale > 0.f ? g->softmax_scale : 1.0f / std::sqrt((float)r.D);
+  r.offs.resize(r.P + 1);
+  if (g->partition_offsets) {
+    for (int p = 0; p <= r.P; ++p) r.offs[p] = g->partition_offsets[p];
+    if (r.offs[0] != 0 || r.offs[r.P] != r.N)
+      return fail(DITA_ERR_SHAPE, "partition offsets must start at 0 and end at tokens");
+    for (int p = 0; p < r.P; ++p)
+      if (r.offs[p + 1] <= r.offs[p])
+        return fail(DITA_ERR_SHAPE, "partition offsets must increase strictly");
+  } else {
+    // numpy array_split rule: the first N mod P partitions hold one extra token
+    const int base = r.N / r.P, extra = r.N % r.P;
+    r.offs[0] = 0;
+    for (int p = 0; p < r.P; ++p) r.offs[p + 1] = r.offs[p] + base + (p < extra ? 1 : 0);
+  }
+  int max_n = 0;
+  r.c2.resize(r.P);
+  r.frame.resize(r.P);
+  r.poffs.resize(r.P + 1);
+  r.poffs[0] = 0;
+  r.num_tiles = 0;
+  for (int p = 0; p < r.P; ++p) {
+    const int n = r.offs[p + 1] - r.offs[p];
+    if (n >= 65536 * 32) return fail(DITA_ERR_SHAPE, "partition too large");
+    max_n = std::max(max_n, n);
+    r.c2[p] = (int64_t)r.offs[p] + r.offs[p + 1] - 1;
+    r.frame[p] = (int32_t)(r.c2[p] / (2 * (int64_t)r.F));
+    r.poffs[p + 1] = r.poffs[p] + (int)align_up(n, dita::kKeyTile);
+    r.num_tiles += (n + r.wg_rows - 1) / r.wg_rows;
+  }
+  r.kt_pad = r.poffs[r.P];
+  r.slot_rows = (int)align_up(max_n, dita::kSlotRowAlign);
+  *out = std::move(r);
+  return ok();
+}
+
+bool tile_active(const Geo& g, int i, int j) {
+  const int fi = g.frame[i], fj = g.frame[j];
+  return fj == fi || fj == 0 || fj == fi - 1 || fj == fi + 1;
+}
+
+// Mask of one step.  `valid` (P*P, may be null) marks slots holding an earlier state;
+// `slot_of` (P*P, may be null) marks blocks that own a cache slot (>= 0).
+dita_status eval_policy(const Geo& g, const dita_block_policy* pol, const uint8_t* valid,
+                        const int32_t* slot_of, std::vector<uint8_t>* out) {
+  if (!pol) return fail(DITA_ERR_INVALID_ARGUMENT, "policy is NULL");
+  const int P = g.P;
+  std::vector<uint8_t> M((size_t)P * P, DITA_SKIP);
+  auto active = [&](int i, int j) { return !pol->tile_sparse || tile_active(g, i, j); };
+  if (pol->kind == DITA_POLICY_EXPLICIT) {
+    if (!pol->explicit_mask) return fail(DITA_ERR_INVALID_ARGUMENT, "explicit_mask is NULL");
+    for (int i = 0; i < P; ++i)
+      for (int j = 0; j < P; ++j) {
+        const uint8_t m = pol->explicit_mask[(size_t)i * P + j];
+        if (m > DITA_REUSE)
+          return fail(DITA_ERR_POLICY, "mask value %d at (%d,%d) outside {0,1,2}", m, i, j);
+        if (m != DITA_SKIP && !active(i, j))
+          return fail(DITA_ERR_POLICY, "block (%d,%d) is outside the tile-sparse set", i, j);
+        M[(size_t)i * P + j] = (pol->anchor && m != DITA_SKIP) ? (uint8_t)DITA_FRESH : m;
+      }
+  } else if (pol->kind == DITA_POLICY_FRAME_THRESHOLD ||
+             pol->kind == DITA_POLICY_CENTROID_THRESHOLD ||
+             pol->kind == DITA_POLICY_FRESH_BUDGET) {
+    if (pol->kind == DITA_POLICY_FRESH_BUDGET &&
+        (pol->reuse_percent < 0 || pol->reuse_percent > 100))
+      return fail(DITA_ERR_INVALID_ARGUMENT, "reuse_percent must be in 0..100");
+    std::vector<int> cand;
+    cand.reserve(P);
+    for (int i = 0; i < P; ++i) {
+      cand.clear();
+      for (int j = 0; j < P; ++j)
+        if (active(i, j)) cand.push_back(j);
+      uint8_t* row = &M[(size_t)i * P];
+      if (pol->anchor) {
+        for (int j : cand) row[j] = DITA_FRESH;
+      } else if (pol->kind == DITA_POLICY_FRAME_THRESHOLD) {
+        for (int j : cand)
+          row[j] = std::abs(g.frame[i] - g.frame[j]) <= pol->max_fresh_frame_dist
+                       ? DITA_FRESH : DITA_REUSE;
+      } else if (pol->kind == DITA_POLICY_CENTROID_THRESHOLD) {
+        for (int j : cand)
+          row[j] = std::llabs(g.c2[i] - g.c2[j]) <= (int64_t)pol->max_fresh_centroid2
+                       ? DITA_FRESH : DITA_REUSE;
+      } else {
+        const int A = (int)cand.size();
+        const int n_reuse = std::min((pol->reuse_percent * A + 50) / 100, A - 1);
+        std::sort(cand.begin(), cand.end(), [&](int a, int b) {
+          const int fa = std::abs(g.frame[i] - g.frame[a]);
+          const int fb = std::abs(g.frame[i] - g.frame[b]);
+          if (fa != fb) return fa < fb;
+          const int64_t ca = std::llabs(g.c2[i] - g.c2[a]);
+          const int64_t cb = std::llabs(g.c2[i] - g.c2[b]);
+          if (ca != cb) return ca < cb;
+          return a < b;
+        });
+        for (int r = 0; r < A; ++r) row[cand[r]] = r < A - n_reuse ? DITA_FRESH : DITA_REUSE;
+      }
+      row[i] = DITA_FRESH;   // the local partition is always computed
+    }
+  } else {
+    return fail(DITA_ERR_INVALID_ARGUMENT, "unknown policy kind %d", pol->kind);
+  }
+  for (int i = 0; i < P; ++i)
+    if (M[(size_t)i * P + i] != DITA_FRESH)
+      return fail(DITA_ERR_POLICY, "diagonal block (%d,%d) must be FRESH", i, i);
+  for (size_t b = 0; b < M.size(); ++b) {
+    if (M[b] == DITA_SKIP) continue;
+    if (slot_of && slot_of[b] < 0)
+      return fail(DITA_ERR_POLICY, "block (%d,%d) has no cache slot (not in the active mask)",
+                  (int)(b / P), (int)(b % P));
+    if (M[b] == DITA_REUSE && (!valid || !valid[b]))
+      return fail(DITA_ERR_CACHE_MISS, "block (%d,%d) is REUSE but its slot holds no state",
+                  (int)(b / P), (int)(b % P));
+  }
+  *out = std::move(M);
+  return ok();
+}
+
+struct Plan {
+  std::vector<uint8_t> mask;
+  std::vector<int32_t> fresh_ptr, fresh_cols, reuse_ptr, reuse_cols;
+  std::array<int32_t, 3> counts{};
+};
+
+void build_lists(int P, const std::vector<uint8_t>& M, Plan* p) {
+  p->mask = M;
+  p->fresh_ptr.assign(1, 0);
+  p->reuse_ptr.assign(1, 0);
+  p->fresh_cols.clear();
+  p->reuse_cols.clear();
+  p->counts = {0, 0, 0};
+  for (int i = 0; i < P; ++i) {
+    for (int j = 0; j < P; ++j) {
+      const uint8_t m = M[(size_t)i * P + j];
+      p->counts[m]++;
+      if (m == DITA_FRESH) p->fresh_cols.push_back(j);
+      if (m == DITA_REUSE) p->reuse_cols.push_back(j);
+    }
+    p->fresh_ptr.push_back((int32_t)p->fresh_cols.size());
+    p->reuse_ptr.push_back((int32_t)p->reuse_cols.size());
+  }
+}
+
+struct Layout {
+  size_t counters = 0, plans = 0, plan_bytes = 0, vt = 0, lse = 0, o = 0, total = 0;
+};
+
+Layout compute_layout(const Geo& g, int num_slots) {
+  Layout L;
+  const size_t P = g.P;
+  const size_t words = dita::kPlanHeader + 2 * (P + 1) + g.num_tiles + 4 * P + 2 * P * P;
+  L.counters = 0;
+  L.plans = 256;
+  L.plan_bytes = align_up(words * 4, 256);
+  size_t at = L.plans + dita::kPlanSlots * L.plan_bytes;
+  const size_t bh = (size_t)g.B * g.H;
+  L.vt = at;
+  if (g.bf16()) at = align_up(at + bh * g.DP * (size_t)g.kt_pad * 2, 256);
+  L.lse = at;
+  at = align_up(at + bh * num_slots * (size_t)g.slot_rows * 4, 256);
+  L.o = at;
+  const size_t esz = g.cache_o == DITA_BF16 ? 2 : 4;
+  at = align_up(at + bh * num_slots * (size_t)g.slot_rows * g.DP * esz, 256);
+  L.total = at;
+  return L;
+}
+
+dita_status slot_table(const Geo& g, const uint8_t* active, std::vector<int32_t>* slot_of,
+                       int* num_slots) {
+  const int P = g.P;
+  slot_of->assign((size_t)P * P, -1);
+  int n = 0;
+  for (int i = 0; i < P; ++i)
+    for (int j = 0; j < P; ++j)
+      if (!active || active[(size_t)i * P + j]) (*slot_of)[(size_t)i * P + j] = n++;
+  for (int i = 0; i < P; ++i)
+    if ((*slot_of)[(size_t)i * P + i] < 0)
+      return fail(DITA_ERR_POLICY, "active mask must contain the diagonal block (%d,%d)", i, i);
+  *num_slots = n;
+  return ok();
+}
+
+struct PlanSlot {
+  bool used = false;
+  std::vector<uint8_t> mask;
+  uint64_t last_use = 0;
+  hipEvent_t event = nullptr;
+  bool event_recorded = false;
+};
+
+}  // namespace
+
+struct dita_cache {
+  Geo g;
+  Layout L;
+  std::vector<int32_t> slot_of;
+  int num_slots = 0;
+  uint8_t* dev = nullptr;
+  size_t dev_bytes = 0;
+  std::vector<uint8_t> valid;        // P*P slot holds a state
+  std::vector<int32_t> last_fresh;   // P*P step at which the slot was written (0 = never)
+  bool has_pending = false;
+  Plan pending;
+  bool has_last = false;
+  Plan last;
+  int64_t steps_done = 0;
+  uint64_t host_fresh = 0, host_reuse = 0;
+  double last_flops = 0, last_rd = 0, last_wr = 0;
+  // device state, created at the first step
+  bool dev_init = false;
+  int device = -1;
+  int32_t* staging = nullptr;        // pinned host, kPlanSlots * plan_bytes
+  PlanSlot pslots[dita::kPlanSlots];
+  uint64_t use_clock = 0;
+};
+
+namespace {
+
+void plan_work(const dita_cache* c, const Plan& p, double* flops, double* rd, double* wr) {
+  const Geo& g = c->g;
+  const double bh = (double)g.B * g.H;
+  const double sc = g.cache_o == DITA_BF16 ? 2.0 : 4.0;
+  double f = 0, r = 0, w = 0;
+  for (int i = 0; i < g.P; ++i) {
+    const double ni = g.offs[i + 1] - g.offs[i];
+    for (int j = 0; j < g.P; ++j) {
+      const uint8_t m = p.mask[(size_t)i * g.P + j];
+      const double nj = g.offs[j + 1] - g.offs[j];
+      if (m == DITA_FRESH) {
+        f += 4.0 * ni * nj * g.D;
+        w += ni * (g.D * sc + 4.0);
+      } else if (m == DITA_REUSE) {
+        r += ni * (g.D * sc + 4.0);
+      }
+    }
+  }
+  *flops = f * bh;
+  *rd = r * bh;
+  *wr = w * bh;
+}
+
+// Device plan words for a mask.
+void encode_plan(const dita_cache* c, const std::vector<uint8_t>& M, int32_t* w) {
+  const Geo& g = c->g;
+  const int P = g.P;
+  int at = dita::kPlanHeader;
+  w[0] = g.num_tiles;
+  w[1] = P;
+  w[3] = 0;
+  for (int p = 0; p <= P; ++p) w[at + p] = g.offs[p];
+  at += P + 1;
+  for (int p = 0; p <= P; ++p) w[at + p] = g.poffs[p];
+  at += P + 1;
+  for (int i = 0; i < P; ++i) {
+    const int n = g.offs[i + 1] - g.offs[i];
+    for (int t = 0; t * g.wg_rows < n; ++t) w[at++] = (i << 16) | t;
+  }
+  const int rows_at = at;
+  int ent_at = rows_at + 4 * P;
+  int e = 0;
+  for (int i = 0; i < P; ++i) {
+    int nf = 0, nr = 0;
+    w[rows_at + 4 * i] = e;
+    for (int kind : {DITA_FRESH, DITA_REUSE})
+      for (int j = 0; j < P; ++j)
+        if (M[(size_t)i * P + j] == kind) {
+          w[ent_at + 2 * e] = j;
+          w[ent_at + 2 * e + 1] = c->slot_of[(size_t)i * P + j];
+          ++e;
+          (kind == DITA_FRESH ? nf : nr)++;
+        }
+    w[rows_at + 4 * i + 1] = nf;
+    w[rows_at + 4 * i + 2] = nr;
+    w[rows_at + 4 * i + 3] = 0;
+  }
+  w[2] = e;
+}
+
+void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
+  const Geo& g = c->g;
+  const int P = g.P;
+  a->vt = c->dev + c->L.vt;
+  a->cache_o = c->dev + c->L.o;
+  a->cache_lse = (float*)(c->dev + c->L.lse);
+  a->counters = (unsigned long long*)(c->dev + c->L.counters);
+  a->plan = (const int32_t*)(c->dev + c->L.plans + (size_t)plan_slot * c->L.plan_bytes);
+  a->off_offs = dita::kPlanHeader;
+  a->off_poffs = a->off_offs + P + 1;
+  a->off_tiles = a->off_poffs + P + 1;
+  a->off_rows = a->off_tiles + g.num_tiles;
+  a->off_ent = a->off_rows + 4 * P;
+  a->B = g.B; a->H = g.H; a->N = g.N; a->D = g.D; a->DP = g.DP; a->P = P;
+  a->num_tiles = g.num_tiles;
+  a->num_slots = c->num_slots;
+  a->slot_rows = g.slot_rows;
+  a->kt_pad = g.kt_pad;
+  a->scale_log2 = g.tau * 1.4426950408889634f;
+}
+
+dita_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DITA_OK;
+  return fail(DITA_ERR_DEVICE, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+dita_status device_init(dita_cache* c, hipStream_t s) {
+  if (c->dev_init) return ok();
+  int dev = -1;
+  dita_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st) return st;
+  void* p = nullptr;
+  st = hip_check(hipHostMalloc(&p, dita::kPlanSlots * c->L.plan_bytes, hipHostMallocDefault),
+                 "hipHostMalloc");
+  if (st) return st;
+  c->staging = (int32_t*)p;
+  for (auto& ps : c->pslots) {
+    st = hip_check(hipEventCreateWithFlags(&ps.event, hipEventDisableTiming), "hipEventCreate");
+    if (st) return st;
+  }
+  st = hip_check(dita::launch_zero_counters(
+                     (unsigned long long*)(c->dev + c->L.counters), 32, s),
+                 "counter clear launch");
+  if (st) return st;
+  c->device = dev;
+  c->dev_init = true;
+  return ok();
+}
+
+// Plan slot holding this mask on the device, uploading it if needed.
+dita_status acquire_plan(dita_cache* c, const std::vector<uint8_t>& M, hipStream_t s,
+                         int* slot) {
+  ++c->use_clock;
+  for (int k = 0; k < dita::kPlanSlots; ++k)
+    if (c->pslots[k].used && c->pslots[k].mask == M) {
+      c->pslots[k].last_use = c->use_clock;
+      *slot = k;
+      return ok();
+    }
+  int victim = 0;
+  for (int k = 0; k < dita::kPlanSlots; ++k) {
+    if (!c->pslots[k].used) { victim = k; break; }
+    if (c->pslots[k].last_use < c->pslots[victim].last_use) victim = k;
+  }
+  PlanSlot& ps = c->pslots[victim];
+  if (ps.event_recorded) {
+    dita_status st = hip_check(hipEventSynchronize(ps.event), "hipEventSynchronize");
+    if (st) return st;
+  }
+  int32_t* host = (int32_t*)((uint8_t*)c->staging + (size_t)victim * c->L.plan_bytes);
+  encode_plan(c, M, host);
+  uint8_t* devp = c->dev + c->L.plans + (size_t)victim * c->L.plan_bytes;
+  dita_status st = hip_check(
+      hipMemcpyAsync(devp, host, c->L.plan_bytes, hipMemcpyHostToDevice, s), "plan upload");
+  if (st) { ps.used = false; return st; }
+  ps.used = true;
+  ps.mask = M;
+  ps.last_use = c->use_clock;
+  *slot = victim;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dita_version(void) { return "dita 0.1 (gfx950)"; }
+
+const char* dita_last_error(void) { return g_err.c_str(); }
+
+dita_status dita_partition_offsets(const dita_geometry* geom, int32_t* out) {
+  if (!out) return fail(DITA_ERR_INVALID_ARGUMENT, "out is NULL");
+  Geo g;
+  dita_status st = resolve_geometry(geom, &g);
+  if (st) return st;
+  std::copy(g.offs.begin(), g.offs.end(), out);
+  return ok();
+}
+
+dita_status dita_policy_mask(const dita_geometry* geom, const dita_block_policy* policy,
+                             const uint8_t* valid, uint8_t* mask_out) {
+  if (!mask_out) return fail(DITA_ERR_INVALID_ARGUMENT, "mask_out is NULL");
+  Geo g;
+  dita_status st = resolve_geometry(geom, &g);
+  if (st) return st;
+  std::vector<uint8_t> M;
+  st = eval_policy(g, policy, valid, nullptr, &M);
+  if (st) return st;
+  std::memcpy(mask_out, M.data(), M.size());
+  return ok();
+}
+
+dita_status dita_cache_required_bytes(const dita_geometry* geom, const uint8_t* active_mask,
+                                      size_t* bytes) {
+  if (!bytes) return fail(DITA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Geo g;
+  dita_status st = resolve_geometry(geom, &g);
+  if (st) return st;
+  std::vector<int32_t> so;
+  int ns = 0;
+  st = slot_table(g, active_mask, &so, &ns);
+  if (st) return st;
+  *bytes = compute_layout(g, ns).total;
+  return ok();
+}
+
+dita_status dita_cache_alloc(const dita_geometry* geom, const uint8_t* active_mask,
+                             void* device_buffer, size_t buffer_bytes, dita_cache** out) {
+  if (!out) return fail(DITA_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (!device_buffer) return fail(DITA_ERR_INVALID_ARGUMENT, "device_buffer is NULL");
+  if ((uintptr_t)device_buffer % 256 != 0)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "device_buffer must be 256-byte aligned");
+  Geo g;
+  dita_status st = resolve_geometry(geom, &g);
+  if (st) return st;
+  std::vector<int32_t> so;
+  int ns = 0;
+  st = slot_table(g, active_mask, &so, &ns);
+  if (st) return st;
+  Layout L = compute_layout(g, ns);
+  if (buffer_bytes < L.total)
+    return fail(DITA_ERR_BUFFER_TOO_SMALL, "buffer holds %zu bytes, %zu needed", buffer_bytes,
+                L.total);
+  dita_cache* c = new (std::nothrow) dita_cache();
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "out of host memory");
+  c->g = std::move(g);
+  c->L = L;
+  c->slot_of = std::move(so);
+  c->num_slots = ns;
+  c->dev = (uint8_t*)device_buffer;
+  c->dev_bytes = buffer_bytes;
+  c->valid.assign((size_t)c->g.P * c->g.P, 0);
+  c->last_fresh.assign((size_t)c->g.P * c->g.P, 0);
+  *out = c;
+  return ok();
+}
+
+dita_status dita_cache_reset(dita_cache* c) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  std::fill(c->valid.begin(), c->valid.end(), 0);
+  std::fill(c->last_fresh.begin(), c->last_fresh.end(), 0);
+  c->has_pending = false;
+  return ok();
+}
+
+dita_status dita_cache_free(dita_cache* c) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (c->dev_init) {
+    for (auto& ps : c->pslots) {
+      if (ps.event_recorded) (void)hipEventSynchronize(ps.event);
+      if (ps.event) (void)hipEventDestroy(ps.event);
+    }
+    if (c->staging) (void)hipHostFree(c->staging);
+  }
+  delete c;
+  return ok();
+}
+
+dita_status dita_set_block_policy(dita_cache* c, const dita_block_policy* policy) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  std::vector<uint8_t> M;
+  dita_status st = eval_policy(c->g, policy, c->valid.data(), c->slot_of.data(), &M);
+  if (st) return st;
+  build_lists(c->g.P, M, &c->pending);
+  c->has_pending = true;
+  return ok();
+}
+
+dita_status dita_get_block_plan(const dita_cache* c, uint8_t* mask, int32_t* fresh_ptr,
+                                int32_t* fresh_cols, int32_t* reuse_ptr, int32_t* reuse_cols,
+                                int32_t* counts) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  const Plan* p = c->has_pending ? &c->pending : (c->has_last ? &c->last : nullptr);
+  if (!p) return fail(DITA_ERR_NO_POLICY, "no policy set and no step executed");
+  if (mask) std::memcpy(mask, p->mask.data(), p->mask.size());
+  if (fresh_ptr) std::copy(p->fresh_ptr.begin(), p->fresh_ptr.end(), fresh_ptr);
+  if (fresh_cols) std::copy(p->fresh_cols.begin(), p->fresh_cols.end(), fresh_cols);
+  if (reuse_ptr) std::copy(p->reuse_ptr.begin(), p->reuse_ptr.end(), reuse_ptr);
+  if (reuse_cols) std::copy(p->reuse_cols.begin(), p->reuse_cols.end(), reuse_cols);
+  if (counts) std::copy(p->counts.begin(), p->counts.end(), counts);
+  return ok();
+}
+
+dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const void* v,
+                           float* out, float* lse_out, void* hip_stream) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!q || !k || !v || !out) return fail(DITA_ERR_INVALID_ARGUMENT, "q, k, v, out required");
+  for (const void* p : {q, k, v, (const void*)out})
+    if ((uintptr_t)p % 16 != 0)
+      return fail(DITA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+  if (lse_out && (uintptr_t)lse_out % 4 != 0)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "lse_out must be 4-byte aligned");
+  if (!c->has_pending) return fail(DITA_ERR_NO_POLICY, "no block policy set for this step");
+  hipStream_t s = (hipStream_t)hip_stream;
+  dita_status st = device_init(c, s);
+  if (st) return st;
+  int pslot = 0;
+  st = acquire_plan(c, c->pending.mask, s, &pslot);
+  if (st) return st;
+  dita::StepArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse_out = lse_out;
+  fill_args(c, pslot, &a);
+  if (c->g.bf16()) {
+    st = hip_check(dita::launch_transpose_v(a, s), "transpose launch");
+    if (st) return st;
+    st = hip_check(dita::launch_step_bf16(a, s), "bf16 step launch");
+  } else {
+    st = hip_check(dita::launch_step_f32(a, s), "f32 step launch");
+  }
+  if (st) return st;
+  st = hip_check(hipEventRecord(c->pslots[pslot].event, s), "hipEventRecord");
+  if (st) return st;
+  c->pslots[pslot].event_recorded = true;
+  // bookkeeping (only after every enqueue succeeded)
+  ++c->steps_done;
+  const size_t PP = (size_t)c->g.P * c->g.P;
+  for (size_t b = 0; b < PP; ++b)
+    if (c->pending.mask[b] == DITA_FRESH) {
+      c->valid[b] = 1;
+      c->last_fresh[b] = (int32_t)c->steps_done;
+    }
+  const uint64_t bh = (uint64_t)c->g.B * c->g.H;
+  c->host_fresh += bh * (uint64_t)c->pending.counts[DITA_FRESH];
+  c->host_reuse += bh * (uint64_t)c->pending.counts[DITA_REUSE];
+  plan_work(c, c->pending, &c->last_flops, &c->last_rd, &c->last_wr);
+  c->last = std::move(c->pending);
+  c->has_last = true;
+  c->has_pending = false;
+  return ok();
+}
+
+dita_status dita_cache_read_slot(dita_cache* c, int32_t b, int32_t h, int32_t i, int32_t j,
+                                 float* o_out, float* lse_out, void* hip_stream) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  const Geo& g = c->g;
+  if (b < 0 || b >= g.B || h < 0 || h >= g.H || i < 0 || i >= g.P || j < 0 || j >= g.P)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "slot index out of range");
+  if (!o_out || !lse_out) return fail(DITA_ERR_INVALID_ARGUMENT, "o_out and lse_out required");
+  const size_t blk = (size_t)i * g.P + j;
+  if (c->slot_of[blk] < 0) return fail(DITA_ERR_POLICY, "block (%d,%d) has no slot", i, j);
+  if (!c->valid[blk]) return fail(DITA_ERR_CACHE_MISS, "slot (%d,%d) holds no state", i, j);
+  dita::StepArgs a{};
+  fill_args(c, 0, &a);
+  return hip_check(dita::launch_read_slot(a, b * g.H + h, c->slot_of[blk],
+                                          g.offs[i + 1] - g.offs[i], o_out, lse_out,
+                                          g.bf16(), (hipStream_t)hip_stream),
+                   "read_slot launch");
+}
+
+dita_status dita_get_stats(const dita_cache* c, dita_step_stats* s) {
+  if (!c || !s) return fail(DITA_ERR_INVALID_ARGUMENT, "cache and stats required");
+  std::memset(s, 0, sizeof *s);
+  s->steps_done = c->steps_done;
+  if (c->has_last)
+    for (int k = 0; k < 3; ++k) s->last_counts[k] = c->last.counts[k];
+  s->host_fresh_blocks = c->host_fresh;
+  s->host_reuse_blocks = c->host_reuse;
+  s->last_fresh_flops = c->last_flops;
+  s->last_cache_read_bytes = c->last_rd;
+  s->last_cache_write_bytes = c->last_wr;
+  if (c->dev_init) {
+    unsigned long long cnt[2] = {0, 0};
+    dita_status st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    if (st) return st;
+    st = hip_check(hipMemcpy(cnt, c->dev + c->L.counters, sizeof cnt, hipMemcpyDeviceToHost),
+                   "counter read");
+    if (st) return st;
+    s->device_fresh_blocks = cnt[0];
+    s->device_reuse_blocks = cnt[1];
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Private interface between the host library (dita_host.cpp) and the HIP kernels
+// (dita_kernels.hip).  Not part of the C ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace dita {
+
+// Keys per K/V tile staged in LDS by the bf16 kernel.
+constexpr int kKeyTile = 64;
+// Waves per workgroup of the bf16 kernel.
+constexpr int kWaves = 4;
+// Query rows per workgroup of the f32 kernel (one row per lane of one wave).
+constexpr int kF32Rows = 64;
+// Cache slots hold their rows padded to a multiple of this.
+constexpr int kSlotRowAlign = 64;
+// Number of device plan slots kept per cache (plans are re-uploaded only on a change).
+constexpr int kPlanSlots = 4;
+
+// Padded head dimension used by the bf16 kernel for a head_dim D (0 = unsupported).
+inline int bf16_padded_dim(int D) {
+  if (D <= 0 || D % 8 != 0 || D > 128) return 0;
+  return D <= 64 ? 64 : (D <= 96 ? 96 : 128);
+}
+// Query sub-tiles of 32 rows held by one wave of the bf16 kernel.
+inline int bf16_subtiles(int DP) { return DP == 64 ? 2 : 1; }
+// Query rows per bf16 workgroup.
+inline int bf16_wg_rows(int DP) { return kWaves * 32 * bf16_subtiles(DP); }
+
+// Layout of one device plan (int32 words), as written by the host and read by the kernels:
+//   [0] num_tiles  [1] P  [2] E (entries)  [3] unused
+//   offs   at kPlanHeader                 : P+1 partition offsets o_p
+//   poffs  at kPlanHeader + (P+1)         : P+1 padded offsets of the transposed-V scratch
+//   tiles  at kPlanHeader + 2(P+1)        : num_tiles words, (i << 16) | tile-in-partition
+//   rows   at tiles + num_tiles           : P x 4 words {first entry, #fresh, #reuse, 0}
+//   ent    at rows + 4P                   : E x 2 words {j, slot}; per row the fresh blocks
+//                                           (ascending j) precede the reused ones
+constexpr int kPlanHeader = 4;
+
+struct StepArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  float* lse_out;            // may be null
+  void* vt;                  // bf16 transposed-V scratch [B*H][DP][kt_pad]
+  void* cache_o;             // bf16: [B*H][slots][slot_rows/32][DP/32][64][16] fragment order
+                             // f32:  [B*H][slots][DP][slot_rows]
+  float* cache_lse;          // [B*H][slots][slot_rows], natural log
+  unsigned long long* counters;  // [0] fresh blocks, [1] reused blocks (cumulative)
+  const int32_t* plan;       // device plan (layout above)
+  int32_t off_offs, off_poffs, off_tiles, off_rows, off_ent;
+  int32_t B, H, N, D, DP, P;
+  int32_t num_tiles;         // workgroup tiles per (b, h)
+  int32_t num_slots;
+  int32_t slot_rows;
+  int32_t kt_pad;            // padded token count of the transposed-V scratch
+  float scale_log2;          // tau * log2(e)
+};
+
+hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s);
+hipError_t launch_transpose_v(const StepArgs& a, hipStream_t s);
+hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s);
+hipError_t launch_step_f32(const StepArgs& a, hipStream_t s);
+hipError_t launch_read_slot(const StepArgs& a, int bh, int slot, int i, float* o_out,
+                            float* lse_out, bool bf16, hipStream_t s);
+
+}  // namespace dita

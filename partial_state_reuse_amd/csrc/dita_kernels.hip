@@ -1,0 +1,583 @@
+// HIP kernels of the dita library for gfx950 (CDNA4, wave64).
+//
+// One step of partitioned attention with selective attention-state reuse (DiTango,
+// gist.science 2607.15650, "State-Centric Parallel Runtime / Composizione dello Stato"):
+// for query partition i, every non-skipped key partition j contributes a state
+// (O_ij, lse_ij); fresh states are recomputed from this step's Q/K/V and written to their
+// cache slot, reused states are read from the slot, and all states of a row are merged by
+// log-sum-exp (associative and commutative, so the order is free).
+//
+// Kernels
+//   transpose_v     V [B,H,N,D] bf16 -> V^T scratch [B*H][DP][kt_pad] bf16, each partition's
+//                   key range padded with zeros to a multiple of the key tile.
+//   step_bf16<DP>   one workgroup (4 waves) per (b, h, query partition i, row tile).  For each
+//                   fresh j: flash-attention over j's keys with bf16 MFMA (S^T = K Q^T, then
+//                   O^T += V^T P^T), K and V^T tiles staged through LDS; at the block's end
+//                   the normalised state goes to the cache (bf16 O, f32 lse) and is folded
+//                   into the row's running merge.  For each reused j the cached state is
+//                   streamed with 16-byte loads and folded the same way.  The epilogue writes
+//                   out = acc / l (f32) and the row lse.
+//   step_f32        the same computation in plain fp32 VALU arithmetic, one lane per row.
+//   read_slot       copies one cache slot out in plain row-major layout.
+//
+// Register layout of the bf16 kernel.  The 32x32x16 bf16 MFMA produces a 32x32 f32 tile in
+// which lane l holds column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 for its 16 registers r.
+// With S^T = K Q^T every lane therefore holds 16 keys of ONE query (l%32), so row max and
+// row sum are in-lane plus one exchange between lanes l and l^32, and O^T = V^T P^T keeps
+// the same one-query-per-lane layout, so the softmax rescale factors never cross lanes.
+// K rows are fed to the MFMA in the order pi(rho) (bits 2 and 3 of the row index swapped),
+// which makes the 8 keys each lane contributes to the P^T operand contiguous, so the V^T
+// operand is one 16-byte LDS read.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "dita_internal.h"
+
+namespace dita {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// max / sum of the values held by lanes l and l^32, in every lane.  (The compiler folds
+// the two results of v_permlane32_swap into one when both operands are the same value, so
+// the exchange goes through ds_bpermute.)
+__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// S^T row index rho -> key position inside a 32-key half: swap bits 2 and 3.
+__device__ __forceinline__ int key_of_row(int rho) {
+  return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+}
+
+// XCD-aware workgroup order: consecutive workgroup ids are dealt round-robin to the 8 XCDs;
+// remap so that each XCD walks a contiguous range of logical work (same head, adjacent rows),
+// which keeps the K/V partitions it shares in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+  const int xcd = bid & 7, idx = bid >> 3, per = G >> 3, rem = G & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// ------------------------------------------------------------------------------------------
+// zero the device counters
+// ------------------------------------------------------------------------------------------
+__global__ void zero_u64(unsigned long long* p, int n) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) p[t] = 0ull;
+}
+
+// ------------------------------------------------------------------------------------------
+// V [B,H,N,D] -> V^T [B*H][DP][kt_pad], zero padded
+// grid (kt_pad / 64, B*H), block 256
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
+  __shared__ uint16_t tile[64][129];   // 64 keys x up to 128 dims (+1 breaks bank conflicts)
+  const int bh = blockIdx.y;
+  const int col0 = blockIdx.x * 64;    // padded key index
+  const int* poffs = a.plan + a.off_poffs;
+  const int* offs = a.plan + a.off_offs;
+  // partition of this 64-key chunk (poffs are multiples of 64)
+  int lo = 0, hi = a.P - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (poffs[mid] <= col0) lo = mid; else hi = mid - 1;
+  }
+  const int p = lo;
+  const int o_p = offs[p], n_p = offs[p + 1] - o_p;
+  const int k0 = col0 - poffs[p];      // first key (partition-relative)
+  const uint16_t* V = (const uint16_t*)a.v + (size_t)bh * a.N * a.D;
+  // load 64 keys x D (8 elements per 16-byte chunk)
+  const int cpr = a.D / 8;             // chunks per row
+  for (int c = threadIdx.x; c < 64 * cpr; c += 256) {
+    const int r = c / cpr, d8 = (c - r * cpr) * 8;
+    const int key = k0 + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (key < n_p) val = ld16(V + (size_t)(o_p + key) * a.D + d8);
+    const uint16_t* e = (const uint16_t*)&val;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) tile[r][d8 + t] = e[t];
+  }
+  __syncthreads();
+  // write DP rows x 64 keys, 8 keys per 16-byte chunk
+  uint16_t* VT = (uint16_t*)a.vt + (size_t)bh * a.DP * a.kt_pad;
+  for (int c = threadIdx.x; c < a.DP * 8; c += 256) {
+    const int d = c >> 3, c8 = (c & 7) * 8;
+    u32x4 val;
+    uint16_t* e = (uint16_t*)&val;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int key = k0 + c8 + t;
+      e[t] = (d < a.D && key < n_p) ? tile[c8 + t][d] : (uint16_t)0;
+    }
+    st16(VT + (size_t)d * a.kt_pad + col0 + c8, val);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 fused step
+// ------------------------------------------------------------------------------------------
+template <int DP, int NST>
+__global__ __launch_bounds__(256) void step_bf16(StepArgs a) {
+  constexpr int NKC = DP / 16;        // 16-wide d chunks of Q K^T
+  constexpr int NDT = DP / 32;        // 32-row d tiles of O^T
+  constexpr int KT = kKeyTile;        // keys per LDS tile
+  constexpr int LDK = DP + 8;         // LDS row stride of the K tile (elements)
+  constexpr int LDV = KT + 8;         // LDS row stride of the V^T tile (elements)
+  constexpr int CH = DP / 32;         // 16-byte chunks per thread per tile (K and V^T alike)
+  constexpr int WG_ROWS = kWaves * NST * 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[KT * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * LDV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h32 = lane >> 5, l32 = lane & 31;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.num_tiles, tix = wg - bh * a.num_tiles;
+  const int* plan = a.plan;
+  const int* offs = plan + a.off_offs;
+  const int* poffs = plan + a.off_poffs;
+  const int packed = plan[a.off_tiles + tix];
+  const int i = packed >> 16, t = packed & 0xffff;
+  const int o_i = offs[i], n_i = offs[i + 1] - o_i;
+  const int row_w = t * WG_ROWS + wave * NST * 32;   // first row of this wave in partition i
+  const int* rinfo = plan + a.off_rows + 4 * i;
+  const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
+  const int* ent = plan + a.off_ent;
+  const size_t bhN = (size_t)bh * a.N;
+  const float sc = a.scale_log2;
+
+  bool live[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) live[st] = row_w + st * 32 < n_i;
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds 8 dims of query row l%32
+  bf16x8 qf[NST][NKC];
+  {
+    const uint16_t* Q = (const uint16_t*)a.q + bhN * a.D;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int r = row_w + st * 32 + l32;
+      const bool ok = r < n_i;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int d0 = kc * 16 + h32 * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok && d0 < a.D) v = ld16(Q + (size_t)(o_i + r) * a.D + d0);
+        qf[st][kc] = as_bf16x8(v);
+      }
+    }
+  }
+
+  // running merge of the row (base-2 units): m = max of lse so far, l = sum of weights
+  f32x16 acc[NST][NDT];
+  float m_row[NST], l_row[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    m_row[st] = kNegInf;
+    l_row[st] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[st][dt] = (f32x16){};
+  }
+
+  const size_t slot_elems = (size_t)a.slot_rows * DP;
+  uint16_t* cache_o = (uint16_t*)a.cache_o;
+  const uint16_t* Kg = (const uint16_t*)a.k + bhN * a.D;
+  const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
+
+  // ---------------- fresh blocks ----------------
+  for (int e = 0; e < nf; ++e) {
+    const int j = ent[2 * (e0 + e)], slot = ent[2 * (e0 + e) + 1];
+    const int o_j = offs[j], n_j = offs[j + 1] - o_j, po_j = poffs[j];
+    const int ntile = (n_j + KT - 1) / KT;
+
+    f32x16 bacc[NST][NDT];
+    float m_b[NST], l_b[NST];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      m_b[st] = kNegInf;
+      l_b[st] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) bacc[st][dt] = (f32x16){};
+    }
+
+    // global -> register prefetch of one K tile and one V^T tile
+    u32x4 pk[CH], pv[CH];
+    auto fetch = [&](int kt) {
+#pragma unroll
+      for (int m = 0; m < CH; ++m) {
+        const int c = tid + 256 * m;
+        const int r = c / (DP / 8), d8 = (c % (DP / 8)) * 8;
+        const int key = kt * KT + r;
+        pk[m] = (u32x4){0u, 0u, 0u, 0u};
+        if (key < n_j && d8 < a.D) pk[m] = ld16(Kg + (size_t)(o_j + key) * a.D + d8);
+        const int d = c >> 3, k8 = (c & 7) * 8;
+        pv[m] = ld16(VTg + (size_t)d * a.kt_pad + po_j + kt * KT + k8);
+      }
+    };
+    fetch(0);
+    for (int kt = 0; kt < ntile; ++kt) {
+      __syncthreads();   // everyone is done reading the previous tile
+#pragma unroll
+      for (int m = 0; m < CH; ++m) {
+        const int c = tid + 256 * m;
+        const int r = c / (DP / 8), d8 = (c % (DP / 8)) * 8;
+        st16(&sK[r * LDK + d8], pk[m]);
+        const int d = c >> 3, k8 = (c & 7) * 8;
+        st16(&sV[d * LDV + k8], pv[m]);
+      }
+      __syncthreads();
+      if (kt + 1 < ntile) fetch(kt + 1);
+
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int kbase = kt * KT + ks * 32;   // first key of this half (partition-relative)
+        if (kbase >= n_j) break;
+        // S^T = K Q^T over this 32-key half
+        f32x16 s[NST];
+#pragma unroll
+        for (int st = 0; st < NST; ++st) s[st] = (f32x16){};
+        const int krow = ks * 32 + key_of_row(l32);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const bf16x8 kf = as_bf16x8(ld16(&sK[krow * LDK + kc * 16 + h32 * 8]));
+#pragma unroll
+          for (int st = 0; st < NST; ++st)
+            if (live[st]) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st][kc], s[st], 0, 0, 0);
+        }
+        const bool tail = kbase + 32 > n_j;
+        bf16x8 pf[NST][2];
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          if (!live[st]) continue;
+          if (tail) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kbase + 16 * (r >> 3) + 8 * h32 + (r & 7);
+              if (key >= n_j) s[st][r] = kNegInf;
+            }
+          }
+          float mx = s[st][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
+          mx = max_halves(mx);
+          const float m_new = fmaxf(m_b[st], mx * sc);
+          const float alpha = fast_exp2(m_b[st] - m_new);
+          m_b[st] = m_new;
+          float psum = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(__builtin_fmaf(s[st][r], sc, -m_new));
+            psum += p;
+            pf[st][r >> 3][r & 7] = (__bf16)p;
+          }
+          l_b[st] = l_b[st] * alpha + psum;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) bacc[st][dt] *= alpha;
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const bf16x8 vf = as_bf16x8(
+                ld16(&sV[(dt * 32 + l32) * LDV + ks * 32 + c * 16 + h32 * 8]));
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+              if (live[st])
+                bacc[st][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st][c], bacc[st][dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // block end: normalise, write the state to its slot, fold it into the row's merge
+    const size_t slot_base = ((size_t)bh * a.num_slots + slot);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (!live[st]) continue;
+      const float lsum = sum_halves(l_b[st]);
+      const float inv = 1.0f / lsum;
+      const float lse2 = m_b[st] + fast_log2(lsum);
+      const int row0 = row_w + st * 32;
+      uint16_t* dst = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        bacc[st][dt] *= inv;
+        u32x4 w0, w1;
+        uint16_t* e0p = (uint16_t*)&w0;
+        uint16_t* e1p = (uint16_t*)&w1;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          e0p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[st][dt][r]);
+          e1p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[st][dt][r + 8]);
+        }
+        st16(dst + dt * 1024 + lane * 16, w0);
+        st16(dst + dt * 1024 + lane * 16 + 8, w1);
+      }
+      if (h32 == 0) a.cache_lse[slot_base * a.slot_rows + row0 + l32] = lse2 * kLn2;
+      const float mn = fmaxf(m_row[st], lse2);
+      const float fa = fast_exp2(m_row[st] - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[st][dt] = acc[st][dt] * fa + bacc[st][dt] * fb;
+      l_row[st] = l_row[st] * fa + fb;
+      m_row[st] = mn;
+    }
+  }
+
+  // ---------------- reused blocks ----------------
+  for (int e = nf; e < nf + nr; ++e) {
+    const int slot = ent[2 * (e0 + e) + 1];
+    const size_t slot_base = ((size_t)bh * a.num_slots + slot);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (!live[st]) continue;
+      const int row0 = row_w + st * 32;
+      const float lse2 = a.cache_lse[slot_base * a.slot_rows + row0 + l32] * kLog2e;
+      const uint16_t* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
+      u32x4 raw[NDT][2];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        raw[dt][0] = ld16(src + dt * 1024 + lane * 16);
+        raw[dt][1] = ld16(src + dt * 1024 + lane * 16 + 8);
+      }
+      const float mn = fmaxf(m_row[st], lse2);
+      const float fa = fast_exp2(m_row[st] - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 lo = as_bf16x8(raw[dt][0]), hi = as_bf16x8(raw[dt][1]);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          acc[st][dt][r] = acc[st][dt][r] * fa + (float)lo[r] * fb;
+          acc[st][dt][r + 8] = acc[st][dt][r + 8] * fa + (float)hi[r] * fb;
+        }
+      }
+      l_row[st] = l_row[st] * fa + fb;
+      m_row[st] = mn;
+    }
+  }
+
+  // ---------------- epilogue: out = acc / l, lse = m + log2(l) ----------------
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    if (!live[st]) continue;
+    const int r = row_w + st * 32 + l32;
+    if (r >= n_i) continue;
+    const float inv = 1.0f / l_row[st];
+    float* orow = a.out + (bhN + o_i + r) * a.D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = dt * 32 + 8 * q4 + 4 * h32;
+        if (d < a.D) {
+          f32x4 v = {acc[st][dt][4 * q4] * inv, acc[st][dt][4 * q4 + 1] * inv,
+                     acc[st][dt][4 * q4 + 2] * inv, acc[st][dt][4 * q4 + 3] * inv};
+          *(f32x4*)(orow + d) = v;
+        }
+      }
+    }
+    if (a.lse_out && h32 == 0)
+      a.lse_out[bhN + o_i + r] = (m_row[st] + fast_log2(l_row[st])) * kLn2;
+  }
+
+  if (t == 0 && tid == 0) {
+    atomicAdd(&a.counters[0], (unsigned long long)nf);
+    atomicAdd(&a.counters[1], (unsigned long long)nr);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// f32 step: one lane per query row, plain fp32 arithmetic (D <= 64, multiple of 4)
+// grid: num_tiles * B*H workgroups of 64 lanes
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void step_f32(StepArgs a) {
+  constexpr int DP = 64;
+  constexpr int KB = 64;                       // keys staged per LDS round
+  __shared__ __attribute__((aligned(16))) float sK[KB][DP];
+  __shared__ __attribute__((aligned(16))) float sV[KB][DP];
+  const int lane = threadIdx.x;
+  const int wg = blockIdx.x;
+  const int bh = wg / a.num_tiles, tix = wg - bh * a.num_tiles;
+  const int* plan = a.plan;
+  const int* offs = plan + a.off_offs;
+  const int packed = plan[a.off_tiles + tix];
+  const int i = packed >> 16, t = packed & 0xffff;
+  const int o_i = offs[i], n_i = offs[i + 1] - o_i;
+  const int r = t * kF32Rows + lane;
+  const bool ok = r < n_i;
+  const int D = a.D;
+  const int* rinfo = plan + a.off_rows + 4 * i;
+  const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
+  const int* ent = plan + a.off_ent;
+  const size_t bhN = (size_t)bh * a.N;
+  const float* Q = (const float*)a.q + bhN * D;
+  const float* K = (const float*)a.k + bhN * D;
+  const float* V = (const float*)a.v + bhN * D;
+  float* cache_o = (float*)a.cache_o;
+
+  float q[DP];
+#pragma unroll
+  for (int d = 0; d < DP; ++d) q[d] = (ok && d < D) ? Q[(size_t)(o_i + r) * D + d] : 0.f;
+  float acc[DP];
+#pragma unroll
+  for (int d = 0; d < DP; ++d) acc[d] = 0.f;
+  float m_row = kNegInf, l_row = 0.f;
+  const float sc = a.scale_log2;
+
+  for (int e = 0; e < nf; ++e) {
+    const int j = ent[2 * (e0 + e)], slot = ent[2 * (e0 + e) + 1];
+    const int o_j = offs[j], n_j = offs[j + 1] - o_j;
+    float b[DP];
+#pragma unroll
+    for (int d = 0; d < DP; ++d) b[d] = 0.f;
+    float m_b = kNegInf, l_b = 0.f;
+    for (int c0 = 0; c0 < n_j; c0 += KB) {
+      __syncthreads();
+      const int key = c0 + lane;
+#pragma unroll 4
+      for (int d = 0; d < DP; ++d) {
+        const bool kv = key < n_j && d < D;
+        sK[lane][d] = kv ? K[(size_t)(o_j + key) * D + d] : 0.f;
+        sV[lane][d] = kv ? V[(size_t)(o_j + key) * D + d] : 0.f;
+      }
+      __syncthreads();
+      const int nk = n_j - c0 < KB ? n_j - c0 : KB;
+      for (int c = 0; c < nk; ++c) {
+        // dot product as four interleaved partial sums of 16 terms
+        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+        for (int d = 0; d < DP; d += 4) {
+          p0 = __builtin_fmaf(q[d], sK[c][d], p0);
+          p1 = __builtin_fmaf(q[d + 1], sK[c][d + 1], p1);
+          p2 = __builtin_fmaf(q[d + 2], sK[c][d + 2], p2);
+          p3 = __builtin_fmaf(q[d + 3], sK[c][d + 3], p3);
+        }
+        const float z = ((p0 + p1) + (p2 + p3)) * sc;
+        const float m_new = fmaxf(m_b, z);
+        const float alpha = fast_exp2(m_b - m_new);
+        const float p = fast_exp2(z - m_new);
+        l_b = l_b * alpha + p;
+#pragma unroll
+        for (int d = 0; d < DP; ++d) b[d] = __builtin_fmaf(p, sV[c][d], b[d] * alpha);
+        m_b = m_new;
+      }
+    }
+    const float lse2 = m_b + fast_log2(l_b);
+    const size_t base = (size_t)bh * a.num_slots + slot;
+    float* dst = cache_o + base * (size_t)DP * a.slot_rows;
+#pragma unroll
+    for (int d = 0; d < DP; ++d) {
+      b[d] = b[d] / l_b;
+      dst[(size_t)d * a.slot_rows + r] = b[d];
+    }
+    a.cache_lse[base * a.slot_rows + r] = lse2 * kLn2;
+    const float mn = fmaxf(m_row, lse2);
+    const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+    for (int d = 0; d < DP; ++d) acc[d] = acc[d] * fa + b[d] * fb;
+    l_row = l_row * fa + fb;
+    m_row = mn;
+  }
+  for (int e = nf; e < nf + nr; ++e) {
+    const int slot = ent[2 * (e0 + e) + 1];
+    const size_t base = (size_t)bh * a.num_slots + slot;
+    const float lse2 = a.cache_lse[base * a.slot_rows + r] * kLog2e;
+    const float* src = cache_o + base * (size_t)DP * a.slot_rows;
+    const float mn = fmaxf(m_row, lse2);
+    const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+    for (int d = 0; d < DP; ++d) acc[d] = acc[d] * fa + src[(size_t)d * a.slot_rows + r] * fb;
+    l_row = l_row * fa + fb;
+    m_row = mn;
+  }
+  if (ok) {
+    float* orow = a.out + (bhN + o_i + r) * D;
+#pragma unroll
+    for (int d = 0; d < DP; ++d)
+      if (d < D) orow[d] = acc[d] / l_row;
+    if (a.lse_out) a.lse_out[bhN + o_i + r] = (m_row + fast_log2(l_row)) * kLn2;
+  }
+  if (t == 0 && lane == 0) {
+    atomicAdd(&a.counters[0], (unsigned long long)nf);
+    atomicAdd(&a.counters[1], (unsigned long long)nr);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// read one cache slot into row-major f32 (n_i x D) and lse (n_i)
+// ------------------------------------------------------------------------------------------
+__global__ void read_slot(StepArgs a, int bh, int slot, int n_i, float* o_out, float* lse_out,
+                          int bf16) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int D = a.D, DP = a.DP;
+  const size_t base = (size_t)bh * a.num_slots + slot;
+  if (idx < n_i) lse_out[idx] = a.cache_lse[base * a.slot_rows + idx];
+  if (idx >= n_i * D) return;
+  const int row = idx / D, d = idx - row * D;
+  float val;
+  if (bf16) {
+    const uint16_t* src = (const uint16_t*)a.cache_o + base * (size_t)a.slot_rows * DP;
+    const int u = row >> 5, l32 = row & 31, dt = d >> 5, dd = d & 31;
+    const int h = (dd >> 2) & 1, reg = 4 * (dd >> 3) + (dd & 3);
+    const int lane = h * 32 + l32;
+    const uint16_t bits = src[(size_t)u * 32 * DP + dt * 1024 + lane * 16 + reg];
+    val = (float)__builtin_bit_cast(__bf16, bits);
+  } else {
+    const float* src = (const float*)a.cache_o + base * (size_t)DP * a.slot_rows;
+    val = src[(size_t)d * a.slot_rows + row];
+  }
+  o_out[idx] = val;
+}
+
+}  // namespace
+
+hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_u64, dim3((n + 63) / 64), dim3(64), 0, s, counters, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_v(const StepArgs& a, hipStream_t s) {
+  dim3 grid(a.kt_pad / kKeyTile, a.B * a.H);
+  hipLaunchKernelGGL(transpose_v, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s) {
+  const int G = a.num_tiles * a.B * a.H;
+  switch (a.DP) {
+    case 64: hipLaunchKernelGGL((step_bf16<64, 2>), dim3(G), dim3(256), 0, s, a); break;
+    case 96: hipLaunchKernelGGL((step_bf16<96, 1>), dim3(G), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((step_bf16<128, 1>), dim3(G), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_step_f32(const StepArgs& a, hipStream_t s) {
+  const int G = a.num_tiles * a.B * a.H;
+  hipLaunchKernelGGL(step_f32, dim3(G), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_slot(const StepArgs& a, int bh, int slot, int n_i, float* o_out,
+                            float* lse_out, bool bf16, hipStream_t s) {
+  const int n = n_i * a.D;
+  hipLaunchKernelGGL(read_slot, dim3((n + 255) / 256), dim3(256), 0, s, a, bh, slot, n_i,
+                     o_out, lse_out, bf16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace dita

@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on identical seeded
+inputs.  Masks, work lists, counts and device-counted blocks are compared bit for bit;
+outputs within max-abs 2e-2 / mean-abs 2e-3 for bf16 inputs and 1e-5 for the f32 workload.
+
+Small geometries compare every output element; the full-size workloads run at their real
+shape in the bench's launch configuration and compare sampled rows (the first two, last two
+and random rows of every partition) of a few heads over every step."""
+import numpy as np
+import pytest
+
+import gpu_helpers as gh
+from gpu_helpers import compare, log
+from workloads import CONFIGS, Policy, custom_config
+from workloads import configs as wcfg
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dita():
+    import partial_state_reuse_amd as d
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return d
+
+
+def oracle_mod():
+    import oracle
+    return oracle
+
+
+def active_for(cfg):
+    from oracle.policy import active_mask, partition_offsets
+    offs = partition_offsets(cfg.tokens, cfg.num_partitions)
+    return active_mask(offs, cfg.frame_tokens, cfg.policy(1).tile_sparse).astype(np.uint8)
+
+
+def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offsets=None,
+                  check_slots=True):
+    """Run every step on the GPU and compare with the oracle on `heads` (and `rows`)."""
+    oracle = oracle_mod()
+    S = steps or cfg.steps
+    bf = cfg.qkv_dtype == "bf16"
+    log(f"case {cfg.name} B={cfg.batch} H={cfg.heads} N={cfg.tokens} D={cfg.head_dim} "
+        f"P={cfg.num_partitions} steps={S} heads={heads} rows={'all' if rows is None else len(rows)}")
+    dev, kept = gh.device_inputs(cfg, S, keep_heads=set(heads))
+    g = dita.geometry_from(cfg, offsets=offsets)
+    cache = dita.Cache(g, active_mask=active_for(cfg) if offsets is None else None)
+    pols = policies or [cfg.policy(s) for s in range(1, S + 1)]
+    outs = []
+    plans = []
+    for s in range(S):
+        cache.set_policy(dita.policy_from(pols[s]))
+        plans.append(cache.plan())
+        q, k, v = dev[s]
+        out, lse = cache.step(q, k, v)
+        sel = torch.as_tensor(rows, device=out.device) if rows is not None else None
+        per_head = {}
+        for (b, h) in heads:
+            o = out[b, h] if sel is None else out[b, h].index_select(0, sel)
+            l = lse[b, h] if sel is None else lse[b, h].index_select(0, sel)
+            per_head[(b, h)] = (o.cpu().numpy(), l.cpu().numpy())
+        outs.append(per_head)
+        if check_slots and s == S - 1:
+            slot_checks = {}
+            for (b, h) in heads[:1]:
+                for (i, j) in [(0, 0), (cfg.num_partitions - 1, cfg.num_partitions - 1)]:
+                    slot_checks[(b, h, i, j)] = [t.cpu().numpy() for t in cache.read_slot(b, h, i, j)]
+    torch.cuda.synchronize()
+    st = cache.stats()
+    ok_all = True
+    worst = (0.0, 0.0)
+    for (b, h) in heads:
+        ref = oracle.run_head(cfg, b, h, steps=S, rows=rows, policies=pols,
+                              inputs=kept[(b, h)], offsets=offsets)
+        for s in range(S):
+            r = ref[s]
+            p = plans[s]
+            assert np.array_equal(p["mask"], r.mask), f"mask step {s + 1}"
+            assert np.array_equal(p["fresh_ptr"], r.fresh_ptr)
+            assert np.array_equal(p["fresh_cols"], r.fresh_cols)
+            assert np.array_equal(p["reuse_ptr"], r.reuse_ptr)
+            assert np.array_equal(p["reuse_cols"], r.reuse_cols)
+            assert np.array_equal(p["counts"], r.counts)
+            o, l = outs[s][(b, h)]
+            ok, mx, mean = compare(o, r.out, bf, f"  b={b} h={h} step {s + 1} out")
+            worst = (max(worst[0], mx), max(worst[1], mean))
+            ok_all &= ok
+            lerr = float(np.max(np.abs(l - r.lse)))
+            assert lerr < (2e-3 if bf else 1e-5), f"lse step {s + 1}: {lerr}"
+        if check_slots and (b, h) == heads[0]:
+            # the last step's cached states of two diagonal blocks (fresh every step)
+            for (bb, hh, i, j), (o_slot, l_slot) in slot_checks.items():
+                offs = oracle.partition_offsets(cfg.tokens, cfg.num_partitions) \
+                    if offsets is None else offsets
+                Qs, Ks, Vs = (np.asarray(x, np.float64) for x in kept[(b, h)][S - 1])
+                sl_i, sl_j = slice(offs[i], offs[i + 1]), slice(offs[j], offs[j + 1])
+                O_ref, l_ref = oracle.block_state(Qs[sl_i], Ks[sl_j], Vs[sl_j],
+                                                  1.0 / np.sqrt(cfg.head_dim))
+                rnd = oracle.round_bf16 if bf else oracle.round_f32
+                ok, _, _ = compare(o_slot, rnd(O_ref), bf, f"  cached state ({i},{j})")
+                assert ok, f"slot ({i},{j})"
+                assert np.max(np.abs(l_slot - l_ref)) < (2e-3 if bf else 1e-5)
+    bh = cfg.batch * cfg.heads
+    assert st["steps_done"] == S
+    assert st["device_fresh_blocks"] == st["host_fresh_blocks"]
+    assert st["device_reuse_blocks"] == st["host_reuse_blocks"]
+    assert st["host_fresh_blocks"] == bh * sum(int(p["counts"][1]) for p in plans)
+    log(f"case {cfg.name}: worst max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e}")
+    assert ok_all
+    cache.free()
+    return outs
+
+
+# --------------------------------------------------------------------------------------
+# small geometries: every element
+# --------------------------------------------------------------------------------------
+def test_tiny_f32_workload_all_heads(dita):
+    cfg = CONFIGS[1]
+    run_and_check(dita, cfg, heads=[(0, 0), (0, 1)])
+
+
+def test_image_bf16_d72_workload(dita):
+    cfg = CONFIGS[2]
+    run_and_check(dita, cfg, heads=[(0, 0), (0, 9), (0, 15)])
+
+
+RAGGED_CASES = [
+    # (name, frames, gh, gw, P, D, heads, steps, policy kind)
+    ("ragged-d64", 3, 10, 13, 5, 64, 2, 3, "budget"),
+    ("ragged-d72", 2, 9, 11, 3, 72, 2, 3, "frame"),
+    ("ragged-d128", 2, 15, 20, 7, 128, 2, 3, "budget"),
+    ("single-partition-d64", 1, 7, 9, 1, 64, 1, 2, "frame"),
+    ("tiny-partitions-d64", 1, 3, 11, 11, 64, 1, 3, "budget"),
+    ("tile-sparse-d64", 6, 5, 7, 6, 64, 2, 4, "tile"),
+    ("video-slice-d64", 2, 45, 80, 8, 64, 2, 3, "budget"),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED_CASES, ids=[c[0] for c in RAGGED_CASES])
+def test_ragged_bf16_geometries(dita, case):
+    name, T, gh_, gw, P, D, H, S, kind = case
+    if kind == "budget":
+        sched = wcfg.AnchorThen(Policy(kind=wcfg.FRESH_BUDGET, reuse_percent=60))
+    elif kind == "frame":
+        sched = wcfg.AnchorThen(Policy(kind=wcfg.FRAME_THRESHOLD, max_fresh_frame_dist=0))
+    else:
+        sched = wcfg.AnchorThen(Policy(kind=wcfg.FRAME_THRESHOLD, max_fresh_frame_dist=1,
+                                       tile_sparse=True))
+    cfg = custom_config(name=name, idx=40, heads=H, head_dim=D, frames=T, grid_h=gh_,
+                        grid_w=gw, num_partitions=P, steps=S, qkv_dtype="bf16",
+                        cache_dtype="bf16", schedule=sched)
+    run_and_check(dita, cfg, heads=[(0, h) for h in range(H)])
+
+
+def test_explicit_masks_and_custom_offsets_bf16(dita):
+    """Explicit masks with skips and ragged hand-picked offsets (including a 1-token and a
+    33-token partition)."""
+    offs = [0, 1, 34, 100, 161, 257, 300]
+    P = 6
+    rng = np.random.default_rng(5)
+    masks = []
+    valid = np.zeros((P, P), bool)
+    for s in range(4):
+        M = rng.integers(0, 3, (P, P)).astype(np.uint8)
+        M[(M == 2) & ~valid] = 1
+        np.fill_diagonal(M, 1)
+        valid |= M == 1
+        masks.append(Policy(kind=wcfg.EXPLICIT, explicit_mask=tuple(int(x) for x in M.ravel())))
+    cfg = custom_config(name="explicit-offsets", idx=41, heads=2, head_dim=64, frames=3,
+                        grid_h=10, grid_w=10, num_partitions=P, steps=4, qkv_dtype="bf16",
+                        cache_dtype="bf16")
+    run_and_check(dita, cfg, heads=[(0, 0), (0, 1)], policies=masks, offsets=offs)
+
+
+def test_f32_random_geometries(dita):
+    for seed, (T, gh_, gw, P, D) in enumerate([(2, 5, 7, 3, 16), (3, 4, 9, 5, 64),
+                                               (1, 10, 10, 7, 40)]):
+        sched = wcfg.AnchorThen(Policy(kind=wcfg.FRESH_BUDGET, reuse_percent=50))
+        cfg = custom_config(name=f"f32-{seed}", idx=42 + seed, heads=2, head_dim=D, frames=T,
+                            grid_h=gh_, grid_w=gw, num_partitions=P, steps=3,
+                            qkv_dtype="f32", cache_dtype="f32", schedule=sched)
+        run_and_check(dita, cfg, heads=[(0, 0), (0, 1)])
+
+
+def test_no_drift_reuse_is_noop_on_gpu(dita):
+    """With unchanged inputs, a reuse step reproduces the all-fresh step (f32 path: within
+    the f32 tolerance; the cached states are the fresh ones)."""
+    cfg = custom_config(name="nodrift", idx=45, heads=2, head_dim=64, frames=4, grid_h=4,
+                        grid_w=8, num_partitions=4, steps=3, qkv_dtype="f32",
+                        cache_dtype="f32", drift=0.0, schedule=CONFIGS[1].schedule)
+    dev, _ = gh.device_inputs(cfg, 3)
+    c = dita.Cache(dita.geometry_from(cfg))
+    res = []
+    for s in range(3):
+        c.set_policy(dita.policy_from(cfg.policy(min(s + 1, 2))))
+        out, _ = c.step(*dev[s])
+        res.append(out.cpu().numpy())
+    assert np.max(np.abs(res[1] - res[0])) <= gh.F32_MAX_ABS
+    assert np.max(np.abs(res[2] - res[0])) <= gh.F32_MAX_ABS
+
+
+def test_determinism_and_side_stream(dita):
+    cfg = CONFIGS[2]
+    dev, _ = gh.device_inputs(cfg, 2)
+    outs = []
+    for use_side in (False, True, True):
+        c = dita.Cache(dita.geometry_from(cfg))
+        stream = torch.cuda.Stream() if use_side else torch.cuda.current_stream()
+        with torch.cuda.stream(stream):
+            for s in range(2):
+                c.set_policy(dita.policy_from(cfg.policy(s + 1)))
+                out, lse = c.step(*dev[s])
+        stream.synchronize()
+        outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+        c.free()
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+
+
+def test_error_paths_on_device(dita):
+    cfg = CONFIGS[1]
+    dev, _ = gh.device_inputs(cfg, 2)
+    c = dita.Cache(dita.geometry_from(cfg))
+    with pytest.raises(dita.DitaError) as e:
+        c.step(*dev[0])
+    assert e.value.name == "NO_POLICY"
+    c.set_policy(dita.policy_from(cfg.policy(1)))
+    c.step(*dev[0])
+    c.set_policy(dita.policy_from(cfg.policy(2)))
+    c.step(*dev[1])
+    c.reset()
+    with pytest.raises(dita.DitaError) as e:
+        c.set_policy(dita.policy_from(cfg.policy(2)))
+    assert e.value.name == "CACHE_MISS"
+    with pytest.raises(dita.DitaError) as e:
+        c.read_slot(0, 0, 0, 3)
+    assert e.value.name == "CACHE_MISS"
+    # recovery: anchor step, then reuse works again
+    c.set_policy(dita.policy_from(cfg.policy(1)))
+    c.step(*dev[0])
+    c.set_policy(dita.policy_from(cfg.policy(2)))
+    c.step(*dev[1])
+    torch.cuda.synchronize()
+    assert c.stats()["steps_done"] == 4
+
+
+# --------------------------------------------------------------------------------------
+# full-size workloads, sampled rows
+# --------------------------------------------------------------------------------------
+def _full(dita, idx, heads, per_part):
+    from oracle.policy import partition_offsets
+    cfg = CONFIGS[idx]
+    rows = gh.sample_rows(partition_offsets(cfg.tokens, cfg.num_partitions), per_part,
+                          np.random.default_rng(idx))
+    run_and_check(dita, cfg, heads=heads, rows=rows)
+
+
+def test_full_video29f_720p(dita):
+    _full(dita, 3, heads=[(0, 0), (0, 13), (0, 23)], per_part=12)
+
+
+def test_full_video93f_tile_sparse(dita):
+    _full(dita, 4, heads=[(0, 0), (0, 23)], per_part=8)
+
+
+def test_full_cfg_long_video_d128(dita):
+    _full(dita, 5, heads=[(0, 0), (0, 39), (1, 0), (1, 39)], per_part=8)

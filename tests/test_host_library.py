@@ -1,0 +1,221 @@
+"""Host logic of libdita on the CPU: exported symbols, partition map, block policy, work
+lists, slot validity and every error code.  Masks, lists and counts must equal the oracle's
+independent builder bit for bit.  No device work is issued (the cache is bound to a dummy
+address, which the library never dereferences before the first step)."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import partial_state_reuse_amd as dita
+from oracle.policy import (FRESH, PolicyError, partition_offsets, policy_mask, work_lists,
+                           active_mask)
+from workloads import CONFIGS, Policy, custom_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7f0000000000          # never dereferenced: no step is run in these tests
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "dita.h")).read()
+    return sorted(set(re.findall(r"\b(dita_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", dita.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(dita.EXPORTED) == names
+
+
+def fake_cache(cfg, active=None):
+    g = dita.geometry_from(cfg)
+    n = dita.dita_cache_required_bytes(g, active)
+    return dita.Cache(g, active_mask=active, buffer_ptr=FAKE, buffer_bytes=n), g
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_offsets_match_oracle(idx):
+    cfg = CONFIGS[idx]
+    g = dita.geometry_from(cfg)
+    assert list(dita.dita_partition_offsets(g)) == partition_offsets(cfg.tokens,
+                                                                     cfg.num_partitions)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_workload_masks_match_oracle(idx):
+    """Every step of every workload (validity as the steps would leave it): mask bit-exact
+    from the standalone evaluator; the first step's CSR lists and counts from a handle."""
+    cfg = CONFIGS[idx]
+    offs = partition_offsets(cfg.tokens, cfg.num_partitions)
+    P = cfg.num_partitions
+    g = dita.geometry_from(cfg)
+    valid = np.zeros((P, P), bool)
+    for s in range(1, cfg.steps + 1):
+        want = policy_mask(offs, cfg.frame_tokens, cfg.policy(s), valid)
+        got = dita.dita_policy_mask(g, dita.policy_from(cfg.policy(s)), valid.astype(np.uint8))
+        assert np.array_equal(got, want), s
+        valid |= want == FRESH
+    act = active_mask(offs, cfg.frame_tokens, cfg.policy(1).tile_sparse).astype(np.uint8)
+    c, _ = fake_cache(cfg, act)
+    c.set_policy(dita.policy_from(cfg.policy(1)))
+    got = c.plan()
+    fp, fc, rp, rc, counts = work_lists(policy_mask(offs, cfg.frame_tokens, cfg.policy(1)))
+    assert np.array_equal(got["fresh_ptr"], fp) and np.array_equal(got["fresh_cols"], fc)
+    assert np.array_equal(got["reuse_ptr"], rp) and np.array_equal(got["reuse_cols"], rc)
+    assert np.array_equal(got["counts"], counts)
+    c.free()
+
+
+def random_geometry(rng):
+    frames = int(rng.integers(1, 6))
+    gh, gw = int(rng.integers(1, 5)), int(rng.integers(1, 6))
+    N = frames * gh * gw
+    P = int(rng.integers(1, min(N, 9) + 1))
+    cfg = custom_config(frames=frames, grid_h=gh, grid_w=gw, num_partitions=P,
+                        head_dim=64, qkv_dtype="bf16", cache_dtype="bf16")
+    if rng.random() < 0.5:
+        cuts = np.sort(rng.choice(np.arange(1, N), size=P - 1, replace=False)) if P > 1 else []
+        offs = [0] + [int(x) for x in cuts] + [N]
+    else:
+        offs = None
+    return cfg, offs
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_policies_match_oracle(seed):
+    rng = np.random.default_rng(seed)
+    cfg, offs = random_geometry(rng)
+    P = cfg.num_partitions
+    o_offs = offs if offs is not None else partition_offsets(cfg.tokens, P)
+    g = dita.geometry_from(cfg, offsets=offs)
+    valid = rng.random((P, P)) < 0.6
+    for trial in range(6):
+        kind = int(rng.integers(0, 4))
+        pol = Policy(kind=kind, max_fresh_frame_dist=int(rng.integers(-1, 3)),
+                     reuse_percent=int(rng.integers(0, 101)),
+                     max_fresh_centroid2=int(rng.integers(-1, 2 * cfg.tokens)),
+                     tile_sparse=bool(rng.random() < 0.4), anchor=bool(rng.random() < 0.2),
+                     explicit_mask=tuple(int(x) for x in rng.integers(0, 3, P * P))
+                     if kind == 0 else None)
+        if kind == 0 and rng.random() < 0.5:
+            m = np.array(pol.explicit_mask).reshape(P, P)
+            np.fill_diagonal(m, 1)
+            pol = Policy(kind=0, explicit_mask=tuple(int(x) for x in m.ravel()),
+                         tile_sparse=False, anchor=pol.anchor)
+        try:
+            want = policy_mask(o_offs, cfg.frame_tokens, pol, valid)
+            want_err = None
+        except PolicyError as e:
+            want, want_err = None, str(e)
+        try:
+            got = dita.dita_policy_mask(g, dita.policy_from(pol), valid.astype(np.uint8))
+            got_err = None
+        except dita.DitaError as e:
+            got, got_err = None, e
+        if want_err is None:
+            assert got_err is None, (pol, got_err)
+            assert np.array_equal(got, want)
+        else:
+            assert got_err is not None and got_err.name in ("POLICY", "CACHE_MISS"), (pol, want_err)
+
+
+def test_handle_bookkeeping_and_errors():
+    cfg = CONFIGS[1]
+    c, g = fake_cache(cfg)
+    # no policy yet
+    with pytest.raises(dita.DitaError) as e:
+        c.plan()
+    assert e.value.name == "NO_POLICY"
+    with pytest.raises(dita.DitaError) as e:
+        c.step_raw(FAKE, FAKE, FAKE, FAKE)
+    assert e.value.name == "NO_POLICY"
+    # reuse before anything was written
+    with pytest.raises(dita.DitaError) as e:
+        c.set_policy(dita.policy_from(cfg.policy(2)))
+    assert e.value.name == "CACHE_MISS"
+    # a failed set keeps the previous pending policy
+    c.set_policy(dita.policy_from(cfg.policy(1)))
+    with pytest.raises(dita.DitaError):
+        c.set_policy(dita.policy_from(cfg.policy(2)))
+    assert c.plan()["counts"].tolist() == [0, 16, 0]
+    # non-fresh diagonal
+    m = np.ones((4, 4), np.uint8)
+    m[2, 2] = 2
+    with pytest.raises(dita.DitaError) as e:
+        c.set_policy(kind=dita.POLICY_EXPLICIT, explicit_mask=m)
+    assert e.value.name == "POLICY"
+    m[2, 2] = 3
+    with pytest.raises(dita.DitaError) as e:
+        c.set_policy(kind=dita.POLICY_EXPLICIT, explicit_mask=m)
+    assert e.value.name == "POLICY"
+    # reset drops the pending policy
+    c.reset()
+    with pytest.raises(dita.DitaError) as e:
+        c.plan()
+    assert e.value.name == "NO_POLICY"
+    # misaligned pointers are rejected before anything is enqueued
+    c.set_policy(dita.policy_from(cfg.policy(1)))
+    with pytest.raises(dita.DitaError) as e:
+        c.step_raw(FAKE + 2, FAKE, FAKE, FAKE)
+    assert e.value.name == "INVALID_ARGUMENT"
+    assert c.stats()["steps_done"] == 0
+    c.free()
+
+
+def test_active_mask_slots():
+    cfg = CONFIGS[4]
+    offs = partition_offsets(cfg.tokens, cfg.num_partitions)
+    act = active_mask(offs, cfg.frame_tokens, True).astype(np.uint8)
+    g = dita.geometry_from(cfg)
+    small = dita.dita_cache_required_bytes(g, act)
+    full = dita.dita_cache_required_bytes(g, None)
+    assert small < full / 4
+    c = dita.Cache(g, active_mask=act, buffer_ptr=FAKE, buffer_bytes=small)
+    # a block outside the active mask has no slot
+    m = np.eye(24, dtype=np.uint8)
+    m[23, 0] = 1
+    m[23, 5] = 1                       # frame distance 18: not in the tile-sparse set
+    with pytest.raises(dita.DitaError) as e:
+        c.set_policy(kind=dita.POLICY_EXPLICIT, explicit_mask=m)
+    assert e.value.name == "POLICY"
+    c.free()
+    with pytest.raises(dita.DitaError) as e:
+        dita.Cache(g, active_mask=act, buffer_ptr=FAKE, buffer_bytes=small - 256)
+    assert e.value.name == "BUFFER_TOO_SMALL"
+    bad = act.copy()
+    bad[3, 3] = 0
+    with pytest.raises(dita.DitaError) as e:
+        dita.dita_cache_required_bytes(g, bad)
+    assert e.value.name == "POLICY"
+
+
+def test_geometry_errors():
+    def err(**kw):
+        base = dict(batch=1, heads=1, tokens=64, head_dim=64, frames=4, grid_h=4, grid_w=4,
+                    num_partitions=4, dtype="bf16")
+        base.update(kw)
+        offsets = base.pop("offsets", None)
+        g = dita.make_geometry(**base, offsets=offsets)
+        with pytest.raises(dita.DitaError) as e:
+            dita.dita_cache_required_bytes(g)
+        return e.value.name
+    assert err(tokens=63) == "SHAPE"
+    assert err(num_partitions=0) == "SHAPE"
+    assert err(num_partitions=65) == "SHAPE"
+    assert err(head_dim=60) == "UNSUPPORTED"
+    assert err(head_dim=136) == "UNSUPPORTED"
+    assert err(dtype="f32", head_dim=128) == "UNSUPPORTED"
+    assert err(offsets=[0, 10, 10, 40, 64]) == "SHAPE"
+    assert err(offsets=[0, 10, 20, 40, 63]) == "SHAPE"
+    assert err(batch=0) == "SHAPE"
+    g = dita.make_geometry(1, 1, 64, 64, 4, 4, 4, 4, "bf16")
+    with pytest.raises(dita.DitaError) as e:
+        dita.Cache(g, buffer_ptr=FAKE + 16, buffer_bytes=1 << 30)
+    assert e.value.name == "INVALID_ARGUMENT"

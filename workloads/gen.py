@@ -149,3 +149,24 @@ def all_steps(cfg: Config, steps: int | None = None, workers: int = 1, drift=Non
                 for t in range(3):
                     out[s][t][b, h] = st[s][t]
     return out
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """uint16 bit patterns of float32 values that are exactly bf16-representable."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    if np.any(u & np.uint32(0xFFFF)):
+        raise ValueError("values are not bf16-representable")
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def head_steps_packed(cfg: Config, b: int, h: int, steps: int | None = None):
+    """Like head_steps, but bf16 workloads come back as uint16 bit patterns (half the
+    bytes to move between processes); f32 workloads as float32."""
+    st = head_steps(cfg, b, h, steps)
+    if cfg.qkv_dtype == "bf16":
+        return [tuple(bf16_bits(x) for x in s) for s in st]
+    return st
