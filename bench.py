@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of one denoising step's partitioned attention with selective state reuse.
+
+Workload: the 29-frame 720p-shaped video (B=1, 24 heads, head_dim 64, 8 latent frames x
+45x80 patches = 28800 tokens, 32 context partitions of 900 tokens, 10 denoising steps:
+an anchor step, then 9 steps with a 40 % fresh budget; bf16 Q/K/V, bf16 O + f32 lse cache,
+f32 output).  Inputs come from the seeded generator and are staged in HBM before timing.
+
+One bench step = one denoising step's attention: the host block policy, the fresh blocks,
+their cache writeback, the reuse fold and the log-sum-exp merge (dita_set_block_policy +
+dita_attn_step).  Steps walk the 10-step schedule cyclically; each cycle starts with a cache
+reset and the anchor step.  With the default step counts (multiples of 10) the timed region
+is whole denoising runs.
+
+Prints one JSON line: dense-equivalent attention TFLOP/s (4 B H N^2 D per step, the cost of
+full attention), ms per step, the dominant kernel's MFMA roofline fraction (fresh-block
+FLOPs / its measured duration), the combined MFMA+HBM roofline of the step, and the fp64
+oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from workloads import CONFIGS  # noqa: E402
+from workloads.gen import head_steps_packed, head_steps  # noqa: E402
+
+METRIC = "dense-equiv attention TFLOP/s + ms/step, % of MFMA+HBM roofline, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+KERNEL_NAME = "step_bf16<64,2>"
+
+
+def _gen_job(args):
+    cfg, b, h, steps = args
+    return b, h, head_steps_packed(cfg, b, h, steps)
+
+
+def _oracle_job(args):
+    """fp64 oracle on one head for `steps` steps; returns its wall time (1 BLAS thread)."""
+    cfg, b, h, steps = args
+    from threadpoolctl import threadpool_limits
+    import oracle
+    inputs = head_steps(cfg, b, h, steps)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.run_head(cfg, b, h, steps=steps, inputs=inputs)
+        return time.perf_counter() - t0
+
+
+def schedule_work(cfg):
+    """Per schedule step: (fresh FLOPs, cache read bytes, cache write bytes), from the
+    library's own policy evaluation (host only)."""
+    import partial_state_reuse_amd as dita
+    g = dita.geometry_from(cfg)
+    offs = dita.dita_partition_offsets(g).astype(np.int64)
+    n = np.diff(offs).astype(np.float64)
+    P = cfg.num_partitions
+    valid = np.zeros((P, P), np.uint8)
+    bh = cfg.batch * cfg.heads
+    D = cfg.head_dim
+    out = []
+    for s in range(1, cfg.steps + 1):
+        M = dita.dita_policy_mask(g, dita.policy_from(cfg.policy(s)), valid)
+        F = M == dita.FRESH
+        R = M == dita.REUSE
+        flops = float(4.0 * D * (n[:, None] * n[None, :])[F].sum()) * bh
+        per_row = n * (D * 2 + 4)
+        rd = float((R * per_row[:, None]).sum()) * bh
+        wr = float((F * per_row[:, None]).sum()) * bh
+        out.append((flops, rd, wr))
+        valid |= F.astype(np.uint8)
+    return out
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in ("dita_kernels.hip", "dita_internal.h"):
+        with open(os.path.join(ROOT, "partial_state_reuse_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(digest):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs,
+    only if they were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "step_bf16_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_digest") != digest:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3,
+                    help="workload number (the bench line is workload 3; others for profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU path only (the step runs every partition on "
+              "one GPU; there is no multi-GPU mode): use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = CONFIGS[args.workload]
+    S = cfg.steps
+    B, H, N, D = cfg.batch, cfg.heads, cfg.tokens, cfg.head_dim
+    # the worker pool is forked before this process touches the GPU
+    pool = mp.get_context("fork").Pool(args.workers)
+    t_gen = time.perf_counter()
+
+    import torch
+    import partial_state_reuse_amd as dita
+
+    bf = cfg.qkv_dtype == "bf16"
+    dt = torch.bfloat16 if bf else torch.float32
+    dev = [[torch.empty((B, H, N, D), dtype=dt, device="cuda") for _ in range(3)]
+           for _ in range(S)]
+    jobs = [(cfg, b, h, S) for b in range(B) for h in range(H)]
+    for b, h, st in pool.imap_unordered(_gen_job, jobs):
+        for s in range(S):
+            for t in range(3):
+                src = torch.from_numpy(st[s][t])
+                dev[s][t][b, h].copy_(src.view(torch.bfloat16) if bf else src)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] inputs staged in HBM: {S} steps x 3 x {B}x{H}x{N}x{D} {cfg.qkv_dtype} "
+          f"({t_gen:.1f} s)", file=sys.stderr, flush=True)
+
+    geom = dita.geometry_from(cfg)
+    # blocks that can ever be non-skip: the anchor step's active set
+    act = (dita.dita_policy_mask(geom, dita.policy_from(cfg.policy(1).as_anchor())) != 0)
+    cache = dita.Cache(geom, active_mask=act.astype(np.uint8))
+    out = torch.empty((B, H, N, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    policies = [dita.policy_from(cfg.policy(s)) for s in range(1, S + 1)]
+    work = schedule_work(cfg)
+    dense_flops = 4.0 * B * H * N * N * D
+    stream = torch.cuda.current_stream()
+
+    def run_step(k):
+        s = k % S
+        if s == 0:
+            cache.reset()
+        cache.set_policy(policies[s])
+        q, kk, v = dev[s]
+        cache.step(q, kk, v, out=out, lse=lse, stream=stream)
+
+    for k in range(args.warmup):
+        run_step(k)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    cache.set_profiling(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(args.warmup, args.warmup + K):
+        run_step(k)
+        ev[k - args.warmup + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = cache.stats()
+    cache.set_profiling(False)
+
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
+    kinds = [(args.warmup + i) % S for i in range(K)]
+    anchor_ms = [m for m, s in zip(step_ms, kinds) if s == 0]
+    steady_ms = [m for m, s in zip(step_ms, kinds) if s != 0]
+    ms_per_step = wall * 1e3 / K
+    value = dense_flops * K / wall / 1e12
+
+    fresh_flops = sum(work[s][0] for s in kinds)
+    cache_bytes = sum(work[s][1] + work[s][2] for s in kinds)
+    kern_ms = st["step_kernel_ms"]
+    prep_ms = st["prep_kernel_ms"]
+    launches = st["profiled_steps"]
+    avg_kernel_ms = kern_ms / max(launches, 1)
+    achieved = fresh_flops / launches / (avg_kernel_ms * 1e-3) / 1e12
+    digest = kernel_source_digest()
+    traffic = measured_traffic(digest)
+    t_roof_sum = sum(work[s][0] / (PEAK_BF16_TFLOPS * 1e12)
+                     + (work[s][1] + work[s][2]) / (PEAK_HBM_GBS * 1e9) for s in kinds)
+    t_roof_max = sum(max(work[s][0] / (PEAK_BF16_TFLOPS * 1e12),
+                         (work[s][1] + work[s][2]) / (PEAK_HBM_GBS * 1e9)) for s in kinds)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic (seeded generator; N(0,1) + 3D sinusoidal position term, "
+                "0.05-sigma drift per step)",
+        "config": {"workload": cfg.name, "batch": B, "heads": H, "tokens": N, "head_dim": D,
+                   "partitions": cfg.num_partitions, "denoise_steps": S,
+                   "schedule": "step 1 anchor (all fresh), then fresh budget 13/32 per row",
+                   "cache": "bf16 O + f32 lse", "out": "f32"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": KERNEL_NAME,
+                     "avg_launch_ms": round(avg_kernel_ms, 4),
+                     "fresh_tflop_per_launch": round(fresh_flops / launches / 1e12, 4),
+                     "kernel_source_digest": digest},
+        "roofline_combined": {
+            "t_roof_ms_per_step": round(t_roof_sum * 1e3 / K, 4),
+            "frac_sum_form": round(t_roof_sum / wall, 4),
+            "frac_max_form": round(t_roof_max / wall, 4),
+            "cache_gb_per_step": round(cache_bytes / K / 1e9, 4)},
+        "breakdown": {
+            "anchor_step_ms": round(float(np.median(anchor_ms)), 4) if anchor_ms else None,
+            "steady_step_ms": round(float(np.median(steady_ms)), 4) if steady_ms else None,
+            "prep_kernel_ms_per_step": round(prep_ms / max(launches, 1), 4),
+            "device_fresh_blocks": st["device_fresh_blocks"],
+            "host_fresh_blocks": st["host_fresh_blocks"]},
+    }
+
+    if not args.no_cpu_baseline:
+        heads = [(0, h) for h in range(min(args.cpu_heads, H))]
+        nsteps = min(args.cpu_steps, S)
+        t1 = time.perf_counter()
+        times = pool.map(_oracle_job, [(cfg, b, h, nsteps) for b, h in heads],
+                         chunksize=1)
+        cpu_wall = max(times)
+        sample_flops = 4.0 * N * N * D * len(heads) * nsteps
+        result["cpu_baseline"] = {
+            "value": round(sample_flops / cpu_wall / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": min(len(heads), args.workers),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, heads {heads[0][1]}..{heads[-1][1]} of {H} "
+                      f"(one process each, 1 BLAS thread), steps 1..{nsteps} of the same "
+                      f"workload (anchor + {nsteps - 1} reuse steps); dense-equivalent "
+                      f"FLOPs of the sample / slowest head's wall time "
+                      f"({cpu_wall:.1f} s; pool wall {time.perf_counter() - t1:.1f} s)"}
+    pool.close()
+    pool.join()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

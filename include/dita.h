@@ -108,6 +108,9 @@ typedef struct dita_step_stats {
   double last_fresh_flops;       /* sum over fresh blocks of 4 n_i n_j D, times B*H          */
   double last_cache_read_bytes;  /* sum over reused blocks of n_i (D*s_c + 4), times B*H     */
   double last_cache_write_bytes; /* sum over fresh blocks of n_i (D*s_c + 4), times B*H      */
+  uint64_t profiled_steps;       /* steps timed since profiling was enabled                  */
+  double step_kernel_ms;         /* summed duration of the main step kernel over those steps */
+  double prep_kernel_ms;         /* summed duration of the V-transpose kernel (bf16 only)    */
 } dita_step_stats;
 
 typedef struct dita_cache dita_cache;
@@ -179,6 +182,11 @@ dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, cons
  * Errors: INVALID_ARGUMENT (indices), POLICY (block without a slot), CACHE_MISS. */
 dita_status dita_cache_read_slot(dita_cache* cache, int32_t b, int32_t h, int32_t i, int32_t j,
                                  float* o_out, float* lse_out, void* hip_stream);
+
+/* Enable (1) or disable (0) kernel timing: the library records HIP events on the launch
+ * stream around each of its kernels and sums their durations into dita_step_stats.
+ * Enabling resets the sums.  Errors: INVALID_ARGUMENT. */
+dita_status dita_set_profiling(dita_cache* cache, int32_t enable);
 
 /* Counters and last-step work.  Synchronises the device to read the device counters. */
 dita_status dita_get_stats(const dita_cache* cache, dita_step_stats* stats);

@@ -2,7 +2,7 @@
 attention-state reuse on MI355X).
 
 Argument marshalling only: every step of the computation runs in the native library
-(`libdita.so`, built in-tree by `python -m partial_state_reuse_amd.build`).  PyTorch is used
+(`libdita.so`, built in-tree by `python partial_state_reuse_amd/build.py`).  PyTorch is used
 for device memory (the cache buffer, outputs) and for the current HIP stream.  If the
 library has not been built, importing this package raises ImportError.
 """
@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdita.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m partial_state_reuse_amd.build`")
+                      "`python partial_state_reuse_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -33,7 +33,7 @@ POLICY_EXPLICIT, POLICY_FRAME_THRESHOLD, POLICY_FRESH_BUDGET, POLICY_CENTROID_TH
 EXPORTED = ["dita_version", "dita_last_error", "dita_policy_mask", "dita_partition_offsets",
             "dita_cache_required_bytes", "dita_cache_alloc", "dita_cache_reset",
             "dita_cache_free", "dita_set_block_policy", "dita_get_block_plan",
-            "dita_attn_step", "dita_cache_read_slot", "dita_get_stats"]
+            "dita_attn_step", "dita_cache_read_slot", "dita_set_profiling", "dita_get_stats"]
 
 
 class DitaError(RuntimeError):
@@ -66,7 +66,9 @@ class StepStats(ctypes.Structure):
                 ("device_fresh_blocks", ctypes.c_uint64), ("device_reuse_blocks", ctypes.c_uint64),
                 ("host_fresh_blocks", ctypes.c_uint64), ("host_reuse_blocks", ctypes.c_uint64),
                 ("last_fresh_flops", ctypes.c_double), ("last_cache_read_bytes", ctypes.c_double),
-                ("last_cache_write_bytes", ctypes.c_double)]
+                ("last_cache_write_bytes", ctypes.c_double),
+                ("profiled_steps", ctypes.c_uint64), ("step_kernel_ms", ctypes.c_double),
+                ("prep_kernel_ms", ctypes.c_double)]
 
 
 _P = ctypes.c_void_p
@@ -89,6 +91,7 @@ _sig = {
     "dita_attn_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "dita_cache_read_slot": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "dita_set_profiling": (ctypes.c_int, [_P, ctypes.c_int32]),
     "dita_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(StepStats)]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -279,6 +282,9 @@ class Cache:
                                          _P(l.data_ptr()), _P(_stream_handle(stream))))
         return o, l
 
+    def set_profiling(self, enable: bool):
+        _check(_lib.dita_set_profiling(self._h, 1 if enable else 0))
+
     def stats(self) -> dict:
         s = StepStats()
         _check(_lib.dita_get_stats(self._h, ctypes.byref(s)))
@@ -289,7 +295,9 @@ class Cache:
                 "host_reuse_blocks": s.host_reuse_blocks,
                 "last_fresh_flops": s.last_fresh_flops,
                 "last_cache_read_bytes": s.last_cache_read_bytes,
-                "last_cache_write_bytes": s.last_cache_write_bytes}
+                "last_cache_write_bytes": s.last_cache_write_bytes,
+                "profiled_steps": s.profiled_steps, "step_kernel_ms": s.step_kernel_ms,
+                "prep_kernel_ms": s.prep_kernel_ms}
 
 
 def policy_from(p) -> BlockPolicy:

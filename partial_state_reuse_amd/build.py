@@ -1,6 +1,8 @@
 """Builds libdita.so in-tree with hipcc for gfx950.
 
-    python -m partial_state_reuse_amd.build
+    python partial_state_reuse_amd/build.py
+
+(Run by path, not as a submodule: importing the package loads the library being rebuilt.)
 
 Every HIP translation unit is compiled with packed-FP32 instructions disabled."""
 from __future__ import annotations

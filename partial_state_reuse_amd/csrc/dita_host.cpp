@@ -274,6 +274,14 @@ dita_status slot_table(const Geo& g, const uint8_t* active, std::vector<int32_t>
   return ok();
 }
 
+// One profiled step: events before the first kernel, between the two kernels, after.
+struct TimedStep {
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  bool pending = false;
+  bool two_kernels = false;
+};
+constexpr int kTimingRing = 64;
+
 struct PlanSlot {
   bool used = false;
   std::vector<uint8_t> mask;
@@ -306,6 +314,12 @@ struct dita_cache {
   int32_t* staging = nullptr;        // pinned host, kPlanSlots * plan_bytes
   PlanSlot pslots[dita::kPlanSlots];
   uint64_t use_clock = 0;
+  // profiling
+  bool profiling = false;
+  TimedStep timing[kTimingRing];
+  int timing_next = 0;
+  uint64_t profiled_steps = 0;
+  double step_ms = 0, prep_ms = 0;
 };
 
 namespace {
@@ -416,6 +430,35 @@ dita_status device_init(dita_cache* c, hipStream_t s) {
   if (st) return st;
   c->device = dev;
   c->dev_init = true;
+  return ok();
+}
+
+// Fold a finished profiled step into the sums.
+dita_status drain_timing(dita_cache* c, TimedStep& t) {
+  if (!t.pending) return ok();
+  dita_status st = hip_check(hipEventSynchronize(t.ev[2]), "hipEventSynchronize");
+  if (st) return st;
+  float a = 0.f, b = 0.f;
+  st = hip_check(hipEventElapsedTime(&a, t.ev[0], t.ev[1]), "hipEventElapsedTime");
+  if (st) return st;
+  st = hip_check(hipEventElapsedTime(&b, t.ev[1], t.ev[2]), "hipEventElapsedTime");
+  if (st) return st;
+  if (t.two_kernels) {
+    c->prep_ms += a;
+    c->step_ms += b;
+  } else {
+    c->step_ms += a + b;
+  }
+  ++c->profiled_steps;
+  t.pending = false;
+  return ok();
+}
+
+dita_status drain_all_timing(dita_cache* c) {
+  for (int k = 0; k < kTimingRing; ++k) {
+    dita_status st = drain_timing(c, c->timing[(c->timing_next + k) % kTimingRing]);
+    if (st) return st;
+  }
   return ok();
 }
 
@@ -537,6 +580,11 @@ dita_status dita_cache_reset(dita_cache* c) {
 
 dita_status dita_cache_free(dita_cache* c) {
   if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  for (auto& t : c->timing) {
+    if (t.pending) (void)hipEventSynchronize(t.ev[2]);
+    for (auto& e : t.ev)
+      if (e) (void)hipEventDestroy(e);
+  }
   if (c->dev_init) {
     for (auto& ps : c->pslots) {
       if (ps.event_recorded) (void)hipEventSynchronize(ps.event);
@@ -592,14 +640,42 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
   dita::StepArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse_out = lse_out;
   fill_args(c, pslot, &a);
+  TimedStep* ts = nullptr;
+  if (c->profiling) {
+    ts = &c->timing[c->timing_next];
+    st = drain_timing(c, *ts);   // the ring slot's previous step must have finished
+    if (st) return st;
+    for (auto& e : ts->ev)
+      if (!e) {
+        st = hip_check(hipEventCreate(&e), "hipEventCreate");
+        if (st) return st;
+      }
+    st = hip_check(hipEventRecord(ts->ev[0], s), "hipEventRecord");
+    if (st) return st;
+  }
   if (c->g.bf16()) {
     st = hip_check(dita::launch_transpose_v(a, s), "transpose launch");
     if (st) return st;
+    if (ts) {
+      st = hip_check(hipEventRecord(ts->ev[1], s), "hipEventRecord");
+      if (st) return st;
+    }
     st = hip_check(dita::launch_step_bf16(a, s), "bf16 step launch");
   } else {
+    if (ts) {
+      st = hip_check(hipEventRecord(ts->ev[1], s), "hipEventRecord");
+      if (st) return st;
+    }
     st = hip_check(dita::launch_step_f32(a, s), "f32 step launch");
   }
   if (st) return st;
+  if (ts) {
+    st = hip_check(hipEventRecord(ts->ev[2], s), "hipEventRecord");
+    if (st) return st;
+    ts->pending = true;
+    ts->two_kernels = c->g.bf16();
+    c->timing_next = (c->timing_next + 1) % kTimingRing;
+  }
   st = hip_check(hipEventRecord(c->pslots[pslot].event, s), "hipEventRecord");
   if (st) return st;
   c->pslots[pslot].event_recorded = true;
@@ -639,8 +715,23 @@ dita_status dita_cache_read_slot(dita_cache* c, int32_t b, int32_t h, int32_t i,
                    "read_slot launch");
 }
 
-dita_status dita_get_stats(const dita_cache* c, dita_step_stats* s) {
-  if (!c || !s) return fail(DITA_ERR_INVALID_ARGUMENT, "cache and stats required");
+dita_status dita_set_profiling(dita_cache* c, int32_t enable) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (enable) {
+    dita_status st = drain_all_timing(c);
+    if (st) return st;
+    c->profiled_steps = 0;
+    c->step_ms = c->prep_ms = 0;
+  }
+  c->profiling = enable != 0;
+  return ok();
+}
+
+dita_status dita_get_stats(const dita_cache* cc, dita_step_stats* s) {
+  if (!cc || !s) return fail(DITA_ERR_INVALID_ARGUMENT, "cache and stats required");
+  dita_cache* c = const_cast<dita_cache*>(cc);   // draining timing events updates sums only
+  dita_status dst = drain_all_timing(c);
+  if (dst) return dst;
   std::memset(s, 0, sizeof *s);
   s->steps_done = c->steps_done;
   if (c->has_last)
@@ -650,6 +741,9 @@ dita_status dita_get_stats(const dita_cache* c, dita_step_stats* s) {
   s->last_fresh_flops = c->last_flops;
   s->last_cache_read_bytes = c->last_rd;
   s->last_cache_write_bytes = c->last_wr;
+  s->profiled_steps = c->profiled_steps;
+  s->step_kernel_ms = c->step_ms;
+  s->prep_kernel_ms = c->prep_ms;
   if (c->dev_init) {
     unsigned long long cnt[2] = {0, 0};
     dita_status st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
