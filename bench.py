@@ -38,7 +38,7 @@ from workloads.gen import head_steps_packed, head_steps  # noqa: E402
 METRIC = "dense-equiv attention TFLOP/s + ms/step, % of MFMA+HBM roofline, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
-KERNEL_NAME = "step_bf16<64,2>"
+KERNEL_NAME = "step_bf16<64>"
 
 
 def _gen_job(args):

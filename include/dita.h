@@ -108,6 +108,10 @@ typedef struct dita_step_stats {
   double last_fresh_flops;       /* sum over fresh blocks of 4 n_i n_j D, times B*H          */
   double last_cache_read_bytes;  /* sum over reused blocks of n_i (D*s_c + 4), times B*H     */
   double last_cache_write_bytes; /* sum over fresh blocks of n_i (D*s_c + 4), times B*H      */
+  uint64_t device_v_range_errors;/* cumulative count of V elements with |v| > 65504: the bf16
+                                    path multiplies P V in fp16, into which every bf16 value of
+                                    that range converts exactly; steps that saw such values are
+                                    not valid                                                 */
   uint64_t profiled_steps;       /* steps timed since profiling was enabled                  */
   double step_kernel_ms;         /* summed duration of the main step kernel over those steps */
   double prep_kernel_ms;         /* summed duration of the V-transpose kernel (bf16 only)    */
@@ -166,7 +170,7 @@ dita_status dita_get_block_plan(const dita_cache* cache, uint8_t* mask, int32_t*
                                 int32_t* counts);
 
 /* Run one denoising step's attention on `hip_stream` (a hipStream_t; NULL = default).
- *   q, k, v   device, [B,H,N,D] of qkv_dtype
+ *   q, k, v   device, [B,H,N,D] of qkv_dtype (bf16: |v| <= 65504, see device_v_range_errors)
  *   out       device, [B,H,N,D] f32: the merged output
  *   lse_out   device, [B,H,N] f32 natural-log L, or NULL
  * Fresh blocks are recomputed and written back to their slots; reused blocks are read from

@@ -67,6 +67,7 @@ class StepStats(ctypes.Structure):
                 ("host_fresh_blocks", ctypes.c_uint64), ("host_reuse_blocks", ctypes.c_uint64),
                 ("last_fresh_flops", ctypes.c_double), ("last_cache_read_bytes", ctypes.c_double),
                 ("last_cache_write_bytes", ctypes.c_double),
+                ("device_v_range_errors", ctypes.c_uint64),
                 ("profiled_steps", ctypes.c_uint64), ("step_kernel_ms", ctypes.c_double),
                 ("prep_kernel_ms", ctypes.c_double)]
 
@@ -296,6 +297,7 @@ class Cache:
                 "last_fresh_flops": s.last_fresh_flops,
                 "last_cache_read_bytes": s.last_cache_read_bytes,
                 "last_cache_write_bytes": s.last_cache_write_bytes,
+                "device_v_range_errors": s.device_v_range_errors,
                 "profiled_steps": s.profiled_steps, "step_kernel_ms": s.step_kernel_ms,
                 "prep_kernel_ms": s.prep_kernel_ms}
 

@@ -18,6 +18,9 @@ LIB = os.path.join(HERE, "libdita.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA results in VGPRs: the softmax and the rescales touch the accumulators with VALU ops,
+# which cannot read AGPRs, so AGPR-resident accumulators cost a copy per element per use.
+MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _run(cmd):
@@ -37,7 +40,7 @@ def build(verbose_resources: bool = False) -> str:
     kern_obj = os.path.join(build_dir, "dita_kernels.o")
     extra = ["-Rpass-analysis=kernel-resource-usage"] if verbose_resources else []
     _run([HIPCC, "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-c",
-          os.path.join(CSRC, "dita_kernels.hip"), "-o", kern_obj] + NO_PACKED_FP32 + inc
+          os.path.join(CSRC, "dita_kernels.hip"), "-o", kern_obj] + NO_PACKED_FP32 + MFMA_VGPR + inc
          + extra)
     objs.append(kern_obj)
     tmp = LIB + ".tmp"

@@ -745,7 +745,7 @@ dita_status dita_get_stats(const dita_cache* cc, dita_step_stats* s) {
   s->step_kernel_ms = c->step_ms;
   s->prep_kernel_ms = c->prep_ms;
   if (c->dev_init) {
-    unsigned long long cnt[2] = {0, 0};
+    unsigned long long cnt[3] = {0, 0, 0};
     dita_status st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
     if (st) return st;
     st = hip_check(hipMemcpy(cnt, c->dev + c->L.counters, sizeof cnt, hipMemcpyDeviceToHost),
@@ -753,6 +753,7 @@ dita_status dita_get_stats(const dita_cache* cc, dita_step_stats* s) {
     if (st) return st;
     s->device_fresh_blocks = cnt[0];
     s->device_reuse_blocks = cnt[1];
+    s->device_v_range_errors = cnt[2];
   }
   return ok();
 }

@@ -24,10 +24,8 @@ inline int bf16_padded_dim(int D) {
   if (D <= 0 || D % 8 != 0 || D > 128) return 0;
   return D <= 64 ? 64 : (D <= 96 ? 96 : 128);
 }
-// Query sub-tiles of 32 rows held by one wave of the bf16 kernel.
-inline int bf16_subtiles(int DP) { return DP == 64 ? 2 : 1; }
-// Query rows per bf16 workgroup.
-inline int bf16_wg_rows(int DP) { return kWaves * 32 * bf16_subtiles(DP); }
+// Query rows per bf16 workgroup (each wave owns a 32-row sub-tile).
+inline int bf16_wg_rows(int /*DP*/) { return kWaves * 32; }
 
 // Layout of one device plan (int32 words), as written by the host and read by the kernels:
 //   [0] num_tiles  [1] P  [2] E (entries)  [3] unused
@@ -45,11 +43,12 @@ struct StepArgs {
   const void* v;
   float* out;
   float* lse_out;            // may be null
-  void* vt;                  // bf16 transposed-V scratch [B*H][DP][kt_pad]
+  void* vt;                  // fp16 transposed-V scratch [B*H][DP][kt_pad]
   void* cache_o;             // bf16: [B*H][slots][slot_rows/32][DP/32][64][16] fragment order
                              // f32:  [B*H][slots][DP][slot_rows]
   float* cache_lse;          // [B*H][slots][slot_rows], natural log
-  unsigned long long* counters;  // [0] fresh blocks, [1] reused blocks (cumulative)
+  unsigned long long* counters;  // [0] fresh blocks, [1] reused blocks, [2] V elements
+                                 // outside the fp16 range (cumulative)
   const int32_t* plan;       // device plan (layout above)
   int32_t off_offs, off_poffs, off_tiles, off_rows, off_ent;
   int32_t B, H, N, D, DP, P;

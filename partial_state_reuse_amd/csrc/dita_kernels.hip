@@ -8,11 +8,11 @@
 // log-sum-exp (associative and commutative, so the order is free).
 //
 // Kernels
-//   transpose_v     V [B,H,N,D] bf16 -> V^T scratch [B*H][DP][kt_pad] bf16, each partition's
+//   transpose_v     V [B,H,N,D] bf16 -> V^T scratch [B*H][DP][kt_pad] fp16, each partition's
 //                   key range padded with zeros to a multiple of the key tile.
 //   step_bf16<DP>   one workgroup (4 waves) per (b, h, query partition i, row tile).  For each
-//                   fresh j: flash-attention over j's keys with bf16 MFMA (S^T = K Q^T, then
-//                   O^T += V^T P^T), K and V^T tiles staged through LDS; at the block's end
+//                   fresh j: flash-attention over j's keys with MFMA (S^T = K Q^T in bf16,
+//                   then O^T += V^T P^T in fp16), K and V^T tiles staged through LDS; at the block's end
 //                   the normalised state goes to the cache (bf16 O, f32 lse) and is folded
 //                   into the row's running merge.  For each reused j the cached state is
 //                   streamed with 16-byte loads and folded the same way.  The epilogue writes
@@ -41,6 +41,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -49,15 +50,25 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// max / sum of the values held by lanes l and l^32, in every lane.  (The compiler folds
-// the two results of v_permlane32_swap into one when both operands are the same value, so
-// the exchange goes through ds_bpermute.)
-__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+// max / sum of the values held by lanes l and l^32, in every lane, through ds_bpermute with
+// the partner's byte address precomputed once.  (v_permlane32_swap would avoid the LDS
+// crossbar, but the compiler substitutes one of its two results for the other when both
+// operands hold the same value, which silently drops the exchange.)
+__device__ __forceinline__ int partner_addr() { return (int)((__lane_id() ^ 32u) << 2); }
+__device__ __forceinline__ float from_partner(float x, int addr) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
+}
+__device__ __forceinline__ float max_halves(float x, int addr) {
+  return fmaxf(x, from_partner(x, addr));
+}
+__device__ __forceinline__ float sum_halves(float x, int addr) {
+  return x + from_partner(x, addr);
+}
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
 // S^T row index rho -> key position inside a 32-key half: swap bits 2 and 3.
 __device__ __forceinline__ int key_of_row(int rho) {
@@ -81,11 +92,15 @@ __global__ void zero_u64(unsigned long long* p, int n) {
 }
 
 // ------------------------------------------------------------------------------------------
-// V [B,H,N,D] -> V^T [B*H][DP][kt_pad], zero padded
+// V [B,H,N,D] bf16 -> V^T [B*H][DP][kt_pad] fp16, zero padded.  Every bf16 value of fp16 range
+// converts exactly (8 significant bits fit in 11; magnitudes below 2^-14 keep an absolute
+// error under 2^-25).  Values beyond the fp16 range are counted in counters[2].
 // grid (kt_pad / 64, B*H), block 256
 // ------------------------------------------------------------------------------------------
+constexpr float kF16Max = 65504.0f;
+
 __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
-  __shared__ uint16_t tile[64][129];   // 64 keys x up to 128 dims (+1 breaks bank conflicts)
+  __shared__ uint16_t tile[64][129];   // 64 keys x up to 128 dims of fp16 (+1 against conflicts)
   const int bh = blockIdx.y;
   const int col0 = blockIdx.x * 64;    // padded key index
   const int* poffs = a.plan + a.off_poffs;
@@ -100,17 +115,23 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
   const int o_p = offs[p], n_p = offs[p + 1] - o_p;
   const int k0 = col0 - poffs[p];      // first key (partition-relative)
   const uint16_t* V = (const uint16_t*)a.v + (size_t)bh * a.N * a.D;
-  // load 64 keys x D (8 elements per 16-byte chunk)
+  // load 64 keys x D (8 elements per 16-byte chunk), converting to fp16
   const int cpr = a.D / 8;             // chunks per row
+  int out_of_range = 0;
   for (int c = threadIdx.x; c < 64 * cpr; c += 256) {
     const int r = c / cpr, d8 = (c - r * cpr) * 8;
     const int key = k0 + r;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (key < n_p) val = ld16(V + (size_t)(o_p + key) * a.D + d8);
-    const uint16_t* e = (const uint16_t*)&val;
+    const bf16x8 b = as_bf16x8(val);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) tile[r][d8 + t] = e[t];
+    for (int t = 0; t < 8; ++t) {
+      const float f = (float)b[t];
+      out_of_range += !(fabsf(f) <= kF16Max);
+      tile[r][d8 + t] = __builtin_bit_cast(uint16_t, (_Float16)f);
+    }
   }
+  if (out_of_range) atomicAdd(&a.counters[2], (unsigned long long)out_of_range);
   __syncthreads();
   // write DP rows x 64 keys, 8 keys per 16-byte chunk
   uint16_t* VT = (uint16_t*)a.vt + (size_t)bh * a.DP * a.kt_pad;
@@ -128,17 +149,25 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 fused step
+// bf16 fused step.  Workgroup = 4 waves = 128 query rows of one partition; each wave owns a
+// 32-row sub-tile (lane l: query row l%32).
 // ------------------------------------------------------------------------------------------
-template <int DP, int NST>
+// Lazy rescale: the running reference m of a block state is raised only when a new logit
+// exceeds it by more than this many powers of two, so p = 2^(s - m) stays <= 2^8 and the
+// accumulator is rescaled rarely (the result is exact either way: m is only a reference).
+constexpr float kRescaleSlack = 8.0f;
+
+template <int DP>
 __global__ __launch_bounds__(256) void step_bf16(StepArgs a) {
   constexpr int NKC = DP / 16;        // 16-wide d chunks of Q K^T
   constexpr int NDT = DP / 32;        // 32-row d tiles of O^T
   constexpr int KT = kKeyTile;        // keys per LDS tile
+  constexpr int NKS = KT / 32;        // 32-key halves per tile
   constexpr int LDK = DP + 8;         // LDS row stride of the K tile (elements)
   constexpr int LDV = KT + 8;         // LDS row stride of the V^T tile (elements)
-  constexpr int CH = DP / 32;         // 16-byte chunks per thread per tile (K and V^T alike)
-  constexpr int WG_ROWS = kWaves * NST * 32;
+  constexpr int CHK = KT * DP / 8 / 256;   // 16-byte chunks per thread per K tile
+  constexpr int CHV = DP * KT / 8 / 256;   // ... per V^T tile
+  constexpr int WG_ROWS = kWaves * 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[KT * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[DP * LDV];
 
@@ -152,45 +181,35 @@ __global__ __launch_bounds__(256) void step_bf16(StepArgs a) {
   const int packed = plan[a.off_tiles + tix];
   const int i = packed >> 16, t = packed & 0xffff;
   const int o_i = offs[i], n_i = offs[i + 1] - o_i;
-  const int row_w = t * WG_ROWS + wave * NST * 32;   // first row of this wave in partition i
+  const int row0 = t * WG_ROWS + wave * 32;     // first row of this wave in partition i
+  const bool live = row0 < n_i;                 // wave-uniform
+  const int myrow = row0 + l32;
   const int* rinfo = plan + a.off_rows + 4 * i;
   const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
   const int* ent = plan + a.off_ent;
   const size_t bhN = (size_t)bh * a.N;
   const float sc = a.scale_log2;
+  const int paddr = partner_addr();
 
-  bool live[NST];
-#pragma unroll
-  for (int st = 0; st < NST; ++st) live[st] = row_w + st * 32 < n_i;
-
-  // Q fragments (B operand of S^T = K Q^T): lane holds 8 dims of query row l%32
-  bf16x8 qf[NST][NKC];
+  // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of query row l%32 per chunk
+  bf16x8 qf[NKC];
   {
     const uint16_t* Q = (const uint16_t*)a.q + bhN * a.D;
+    const bool ok = myrow < n_i;
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      const int r = row_w + st * 32 + l32;
-      const bool ok = r < n_i;
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const int d0 = kc * 16 + h32 * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok && d0 < a.D) v = ld16(Q + (size_t)(o_i + r) * a.D + d0);
-        qf[st][kc] = as_bf16x8(v);
-      }
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int d0 = kc * 16 + h32 * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok && d0 < a.D) v = ld16(Q + (size_t)(o_i + myrow) * a.D + d0);
+      qf[kc] = as_bf16x8(v);
     }
   }
 
-  // running merge of the row (base-2 units): m = max of lse so far, l = sum of weights
-  f32x16 acc[NST][NDT];
-  float m_row[NST], l_row[NST];
+  // running merge of the row (base-2 units)
+  f32x16 acc[NDT];
 #pragma unroll
-  for (int st = 0; st < NST; ++st) {
-    m_row[st] = kNegInf;
-    l_row[st] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[st][dt] = (f32x16){};
-  }
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x16){};
+  float m_row = kNegInf, l_row = 0.f;
 
   const size_t slot_elems = (size_t)a.slot_rows * DP;
   uint16_t* cache_o = (uint16_t*)a.cache_o;
@@ -203,27 +222,25 @@ __global__ __launch_bounds__(256) void step_bf16(StepArgs a) {
     const int o_j = offs[j], n_j = offs[j + 1] - o_j, po_j = poffs[j];
     const int ntile = (n_j + KT - 1) / KT;
 
-    f32x16 bacc[NST][NDT];
-    float m_b[NST], l_b[NST];
+    f32x16 bacc[NDT];
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      m_b[st] = kNegInf;
-      l_b[st] = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) bacc[st][dt] = (f32x16){};
-    }
+    for (int dt = 0; dt < NDT; ++dt) bacc[dt] = (f32x16){};
+    float m_b = kNegInf, l_b = 0.f;   // l_b: this lane's partial sum (16 of the 32 keys)
 
-    // global -> register prefetch of one K tile and one V^T tile
-    u32x4 pk[CH], pv[CH];
+    u32x4 pk[CHK], pv[CHV];
     auto fetch = [&](int kt) {
 #pragma unroll
-      for (int m = 0; m < CH; ++m) {
+      for (int m = 0; m < CHK; ++m) {
         const int c = tid + 256 * m;
         const int r = c / (DP / 8), d8 = (c % (DP / 8)) * 8;
         const int key = kt * KT + r;
         pk[m] = (u32x4){0u, 0u, 0u, 0u};
         if (key < n_j && d8 < a.D) pk[m] = ld16(Kg + (size_t)(o_j + key) * a.D + d8);
-        const int d = c >> 3, k8 = (c & 7) * 8;
+      }
+#pragma unroll
+      for (int m = 0; m < CHV; ++m) {
+        const int c = tid + 256 * m;
+        const int d = c / (KT / 8), k8 = (c % (KT / 8)) * 8;
         pv[m] = ld16(VTg + (size_t)d * a.kt_pad + po_j + kt * KT + k8);
       }
     };
@@ -231,166 +248,153 @@ __global__ __launch_bounds__(256) void step_bf16(StepArgs a) {
     for (int kt = 0; kt < ntile; ++kt) {
       __syncthreads();   // everyone is done reading the previous tile
 #pragma unroll
-      for (int m = 0; m < CH; ++m) {
+      for (int m = 0; m < CHK; ++m) {
         const int c = tid + 256 * m;
-        const int r = c / (DP / 8), d8 = (c % (DP / 8)) * 8;
-        st16(&sK[r * LDK + d8], pk[m]);
-        const int d = c >> 3, k8 = (c & 7) * 8;
-        st16(&sV[d * LDV + k8], pv[m]);
+        st16(&sK[(c / (DP / 8)) * LDK + (c % (DP / 8)) * 8], pk[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < CHV; ++m) {
+        const int c = tid + 256 * m;
+        st16(&sV[(c / (KT / 8)) * LDV + (c % (KT / 8)) * 8], pv[m]);
       }
       __syncthreads();
       if (kt + 1 < ntile) fetch(kt + 1);
+      if (!live) continue;
 
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {
         const int kbase = kt * KT + ks * 32;   // first key of this half (partition-relative)
         if (kbase >= n_j) break;
         // S^T = K Q^T over this 32-key half
-        f32x16 s[NST];
-#pragma unroll
-        for (int st = 0; st < NST; ++st) s[st] = (f32x16){};
+        f32x16 s = (f32x16){};
         const int krow = ks * 32 + key_of_row(l32);
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
           const bf16x8 kf = as_bf16x8(ld16(&sK[krow * LDK + kc * 16 + h32 * 8]));
-#pragma unroll
-          for (int st = 0; st < NST; ++st)
-            if (live[st]) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st][kc], s[st], 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s, 0, 0, 0);
         }
-        const bool tail = kbase + 32 > n_j;
-        bf16x8 pf[NST][2];
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-          if (!live[st]) continue;
-          if (tail) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kbase + 16 * (r >> 3) + 8 * h32 + (r & 7);
-              if (key >= n_j) s[st][r] = kNegInf;
-            }
-          }
-          float mx = s[st][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
-          mx = max_halves(mx);
-          const float m_new = fmaxf(m_b[st], mx * sc);
-          const float alpha = fast_exp2(m_b[st] - m_new);
-          m_b[st] = m_new;
-          float psum = 0.f;
+        if (kbase + 32 > n_j) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(__builtin_fmaf(s[st][r], sc, -m_new));
-            psum += p;
-            pf[st][r >> 3][r & 7] = (__bf16)p;
+            const int key = kbase + 16 * (r >> 3) + 8 * h32 + (r & 7);
+            if (key >= n_j) s[r] = kNegInf;
           }
-          l_b[st] = l_b[st] * alpha + psum;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) bacc[st][dt] *= alpha;
         }
+        float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+        for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1 < 16 ? r + 1 : r]);
+        mx = max_halves(mx, paddr) * sc;
+        if (__any(mx > m_b + kRescaleSlack)) {
+          const float m_new = fmaxf(m_b, mx);
+          const float alpha = fast_exp2(m_b - m_new);
+          m_b = m_new;
+          l_b *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= alpha;
+        }
+        // p in fp32 for the row sum (the lse is cached and reused, so it is kept to fp32
+        // accuracy), rounded to fp16 as the MFMA operand: p <= 2^8 after the lazy rescale,
+        // and fp16's 11 significant bits keep the PV product 8x closer than bf16 would
+        f16x8 pf[2];
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[r], sc, -m_b));
+          const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], sc, -m_b));
+          ps0 += p0;
+          ps1 += p1;
+          pf[r >> 3][r & 7] = (_Float16)p0;
+          pf[r >> 3][(r & 7) + 1] = (_Float16)p1;
+        }
+        l_b += ps0 + ps1;
         // O^T += V^T P^T
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const bf16x8 vf = as_bf16x8(
+            const f16x8 vf = as_f16x8(
                 ld16(&sV[(dt * 32 + l32) * LDV + ks * 32 + c * 16 + h32 * 8]));
-#pragma unroll
-            for (int st = 0; st < NST; ++st)
-              if (live[st])
-                bacc[st][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st][c], bacc[st][dt], 0, 0, 0);
+            bacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], bacc[dt], 0, 0, 0);
           }
-        }
       }
     }
+    if (!live) continue;
 
     // block end: normalise, write the state to its slot, fold it into the row's merge
-    const size_t slot_base = ((size_t)bh * a.num_slots + slot);
+    const size_t slot_base = (size_t)bh * a.num_slots + slot;
+    const float lsum = sum_halves(l_b, paddr);
+    const float inv = 1.0f / lsum;
+    const float lse2 = m_b + fast_log2(lsum);
+    uint16_t* dst = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      if (!live[st]) continue;
-      const float lsum = sum_halves(l_b[st]);
-      const float inv = 1.0f / lsum;
-      const float lse2 = m_b[st] + fast_log2(lsum);
-      const int row0 = row_w + st * 32;
-      uint16_t* dst = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
+    for (int dt = 0; dt < NDT; ++dt) {
+      bacc[dt] *= inv;
+      u32x4 w0, w1;
+      uint16_t* e0p = (uint16_t*)&w0;
+      uint16_t* e1p = (uint16_t*)&w1;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        bacc[st][dt] *= inv;
-        u32x4 w0, w1;
-        uint16_t* e0p = (uint16_t*)&w0;
-        uint16_t* e1p = (uint16_t*)&w1;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          e0p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[st][dt][r]);
-          e1p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[st][dt][r + 8]);
-        }
-        st16(dst + dt * 1024 + lane * 16, w0);
-        st16(dst + dt * 1024 + lane * 16 + 8, w1);
+      for (int r = 0; r < 8; ++r) {
+        e0p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][r]);
+        e1p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][r + 8]);
       }
-      if (h32 == 0) a.cache_lse[slot_base * a.slot_rows + row0 + l32] = lse2 * kLn2;
-      const float mn = fmaxf(m_row[st], lse2);
-      const float fa = fast_exp2(m_row[st] - mn), fb = fast_exp2(lse2 - mn);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[st][dt] = acc[st][dt] * fa + bacc[st][dt] * fb;
-      l_row[st] = l_row[st] * fa + fb;
-      m_row[st] = mn;
+      st16(dst + dt * 1024 + lane * 16, w0);
+      st16(dst + dt * 1024 + lane * 16 + 8, w1);
     }
+    if (h32 == 0) a.cache_lse[slot_base * a.slot_rows + myrow] = lse2 * kLn2;
+    const float mn = fmaxf(m_row, lse2);
+    const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * fa + bacc[dt] * fb;
+    l_row = l_row * fa + fb;
+    m_row = mn;
   }
+  if (!live) return;
 
   // ---------------- reused blocks ----------------
   for (int e = nf; e < nf + nr; ++e) {
     const int slot = ent[2 * (e0 + e) + 1];
-    const size_t slot_base = ((size_t)bh * a.num_slots + slot);
+    const size_t slot_base = (size_t)bh * a.num_slots + slot;
+    const float lse2 = a.cache_lse[slot_base * a.slot_rows + myrow] * kLog2e;
+    const uint16_t* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
+    u32x4 raw[NDT][2];
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      if (!live[st]) continue;
-      const int row0 = row_w + st * 32;
-      const float lse2 = a.cache_lse[slot_base * a.slot_rows + row0 + l32] * kLog2e;
-      const uint16_t* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
-      u32x4 raw[NDT][2];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        raw[dt][0] = ld16(src + dt * 1024 + lane * 16);
-        raw[dt][1] = ld16(src + dt * 1024 + lane * 16 + 8);
-      }
-      const float mn = fmaxf(m_row[st], lse2);
-      const float fa = fast_exp2(m_row[st] - mn), fb = fast_exp2(lse2 - mn);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8 lo = as_bf16x8(raw[dt][0]), hi = as_bf16x8(raw[dt][1]);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          acc[st][dt][r] = acc[st][dt][r] * fa + (float)lo[r] * fb;
-          acc[st][dt][r + 8] = acc[st][dt][r + 8] * fa + (float)hi[r] * fb;
-        }
-      }
-      l_row[st] = l_row[st] * fa + fb;
-      m_row[st] = mn;
+    for (int dt = 0; dt < NDT; ++dt) {
+      raw[dt][0] = ld16(src + dt * 1024 + lane * 16);
+      raw[dt][1] = ld16(src + dt * 1024 + lane * 16 + 8);
     }
+    const float mn = fmaxf(m_row, lse2);
+    const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x8 lo = as_bf16x8(raw[dt][0]), hi = as_bf16x8(raw[dt][1]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        acc[dt][r] = acc[dt][r] * fa + (float)lo[r] * fb;
+        acc[dt][r + 8] = acc[dt][r + 8] * fa + (float)hi[r] * fb;
+      }
+    }
+    l_row = l_row * fa + fb;
+    m_row = mn;
   }
 
   // ---------------- epilogue: out = acc / l, lse = m + log2(l) ----------------
-#pragma unroll
-  for (int st = 0; st < NST; ++st) {
-    if (!live[st]) continue;
-    const int r = row_w + st * 32 + l32;
-    if (r >= n_i) continue;
-    const float inv = 1.0f / l_row[st];
-    float* orow = a.out + (bhN + o_i + r) * a.D;
+  if (myrow < n_i) {
+    const float inv = 1.0f / l_row;
+    float* orow = a.out + (bhN + o_i + myrow) * a.D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = dt * 32 + 8 * q4 + 4 * h32;
         if (d < a.D) {
-          f32x4 v = {acc[st][dt][4 * q4] * inv, acc[st][dt][4 * q4 + 1] * inv,
-                     acc[st][dt][4 * q4 + 2] * inv, acc[st][dt][4 * q4 + 3] * inv};
+          f32x4 v = {acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
+                     acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv};
           *(f32x4*)(orow + d) = v;
         }
       }
     }
     if (a.lse_out && h32 == 0)
-      a.lse_out[bhN + o_i + r] = (m_row[st] + fast_log2(l_row[st])) * kLn2;
+      a.lse_out[bhN + o_i + myrow] = (m_row + fast_log2(l_row)) * kLn2;
   }
 
   if (t == 0 && tid == 0) {
@@ -558,9 +562,9 @@ hipError_t launch_transpose_v(const StepArgs& a, hipStream_t s) {
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s) {
   const int G = a.num_tiles * a.B * a.H;
   switch (a.DP) {
-    case 64: hipLaunchKernelGGL((step_bf16<64, 2>), dim3(G), dim3(256), 0, s, a); break;
-    case 96: hipLaunchKernelGGL((step_bf16<96, 1>), dim3(G), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((step_bf16<128, 1>), dim3(G), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((step_bf16<64>), dim3(G), dim3(256), 0, s, a); break;
+    case 96: hipLaunchKernelGGL((step_bf16<96>), dim3(G), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((step_bf16<128>), dim3(G), dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
