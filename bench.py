@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (outside the timed "
+                         "region) as the reference for hardware traffic counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -171,6 +174,13 @@ def main():
     for k in range(args.warmup):
         run_step(k)
     torch.cuda.synchronize()
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src_c = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst_c = torch.empty_like(src_c)
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
 
     K = args.steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
