@@ -42,6 +42,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -64,6 +65,13 @@ __device__ __forceinline__ float max_halves(float x, int addr) {
 __device__ __forceinline__ float sum_halves(float x, int addr) {
   return x + from_partner(x, addr);
 }
+
+// The device plan is written by the host before the launch and never by a kernel, so it is
+// read through the constant address space: uniform reads become scalar loads, which are
+// counted separately from the vector loads in flight (a vector read of the plan would make
+// the wave wait for every outstanding prefetch).
+typedef __attribute__((address_space(4))) const int32_t cint;
+__device__ __forceinline__ const cint* as_const(const int32_t* p) { return (const cint*)p; }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
 constexpr float kRescaleSlack = 8.0f;
 
 template <int DP>
-__global__ __launch_bounds__(256) void step_bf16(StepArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 3 : 1))) void step_bf16(StepArgs a) {
   constexpr int NKC = DP / 16;        // 16-wide d chunks of Q K^T
   constexpr int NDT = DP / 32;        // 32-row d tiles of O^T
   constexpr int KT = kKeyTile;        // keys per LDS tile
@@ -175,21 +183,22 @@ __global__ __launch_bounds__(256) void step_bf16(StepArgs a) {
   const int h32 = lane >> 5, l32 = lane & 31;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / a.num_tiles, tix = wg - bh * a.num_tiles;
-  const int* plan = a.plan;
-  const int* offs = plan + a.off_offs;
-  const int* poffs = plan + a.off_poffs;
+  const cint* plan = as_const(a.plan);
+  const cint* offs = plan + a.off_offs;
+  const cint* poffs = plan + a.off_poffs;
   const int packed = plan[a.off_tiles + tix];
   const int i = packed >> 16, t = packed & 0xffff;
   const int o_i = offs[i], n_i = offs[i + 1] - o_i;
   const int row0 = t * WG_ROWS + wave * 32;     // first row of this wave in partition i
   const bool live = row0 < n_i;                 // wave-uniform
   const int myrow = row0 + l32;
-  const int* rinfo = plan + a.off_rows + 4 * i;
+  const cint* rinfo = plan + a.off_rows + 4 * i;
   const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
-  const int* ent = plan + a.off_ent;
+  const cint* ent = plan + a.off_ent;
   const size_t bhN = (size_t)bh * a.N;
   const float sc = a.scale_log2;
   const int paddr = partner_addr();
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of query row l%32 per chunk
   bf16x8 qf[NKC];
@@ -233,9 +242,8 @@ __global__ __launch_bounds__(256) void step_bf16(StepArgs a) {
       for (int m = 0; m < CHK; ++m) {
         const int c = tid + 256 * m;
         const int r = c / (DP / 8), d8 = (c % (DP / 8)) * 8;
-        const int key = kt * KT + r;
-        pk[m] = (u32x4){0u, 0u, 0u, 0u};
-        if (key < n_j && d8 < a.D) pk[m] = ld16(Kg + (size_t)(o_j + key) * a.D + d8);
+        const int key = min(kt * KT + r, n_j - 1);
+        pk[m] = ld16(Kg + (size_t)(o_j + key) * a.D + min(d8, a.D - 8));
       }
 #pragma unroll
       for (int m = 0; m < CHV; ++m) {
@@ -292,21 +300,17 @@ __global__ __launch_bounds__(256) void step_bf16(StepArgs a) {
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= alpha;
         }
-        // p in fp32 for the row sum (the lse is cached and reused, so it is kept to fp32
-        // accuracy), rounded to fp16 as the MFMA operand: p <= 2^8 after the lazy rescale,
-        // and fp16's 11 significant bits keep the PV product 8x closer than bf16 would
         f16x8 pf[2];
-        float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[r], sc, -m_b));
-          const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], sc, -m_b));
-          ps0 += p0;
-          ps1 += p1;
-          pf[r >> 3][r & 7] = (_Float16)p0;
-          pf[r >> 3][(r & 7) + 1] = (_Float16)p1;
-        }
-        l_b += ps0 + ps1;
+        for (int r = 0; r < 16; ++r)
+          pf[r >> 3][r & 7] = (_Float16)fast_exp2(__builtin_fmaf(s[r], sc, -m_b));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            const f16x2 pair = {pf[c][2 * q2], pf[c][2 * q2 + 1]};
+            l_b = __builtin_amdgcn_fdot2(pair, ones, l_b, false);
+          }
         // O^T += V^T P^T
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
