@@ -54,7 +54,10 @@ struct Geo {
   std::vector<int32_t> poffs;   // P+1 padded offsets (multiples of the key tile)
   int kt_pad = 0;
   int wg_rows = 0;
-  int num_tiles = 0;
+  int num_tiles = 0;                 // workgroups per (b, h): tail workgroups, then groups
+  int num_tail_wg = 0;               // tail workgroups per (b, h)
+  std::vector<int32_t> groups;       // per partition: row groups run by 4-wave workgroups
+  std::vector<int32_t> tails;        // {i, first row} per tail sub-tile, padded to 4 per wg
   int slot_rows = 0;
   bool bf16() const { return qkv == DITA_BF16; }
 };
@@ -112,7 +115,8 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
   r.frame.resize(r.P);
   r.poffs.resize(r.P + 1);
   r.poffs[0] = 0;
-  r.num_tiles = 0;
+  r.groups.resize(r.P);
+  int num_groups = 0;
   for (int p = 0; p < r.P; ++p) {
     const int n = r.offs[p + 1] - r.offs[p];
     if (n >= 65536 * 32) return fail(DITA_ERR_SHAPE, "partition too large");
@@ -120,8 +124,29 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
     r.c2[p] = (int64_t)r.offs[p] + r.offs[p + 1] - 1;
     r.frame[p] = (int32_t)(r.c2[p] / (2 * (int64_t)r.F));
     r.poffs[p + 1] = r.poffs[p] + (int)align_up(n, dita::kKeyTile);
-    r.num_tiles += (n + r.wg_rows - 1) / r.wg_rows;
+    // Row groups of wg_rows rows.  On the bf16 path a last group that would keep at most
+    // kMaxTailSubtiles of its 4 waves busy becomes tail sub-tiles instead: they run as
+    // independent waves, 4 to a workgroup, so no wave slot idles on an empty sub-tile.
+    int full = n / r.wg_rows;
+    const int rem = n - full * r.wg_rows;
+    const int sub = (rem + 31) / 32;
+    if (rem > 0 && r.bf16() && sub <= dita::kMaxTailSubtiles) {
+      for (int s = 0; s < sub; ++s) {
+        r.tails.push_back(p);
+        r.tails.push_back(full * r.wg_rows + 32 * s);
+      }
+    } else if (rem > 0) {
+      ++full;
+    }
+    r.groups[p] = full;
+    num_groups += full;
   }
+  while (r.tails.size() % 8) {
+    r.tails.push_back(-1);
+    r.tails.push_back(0);
+  }
+  r.num_tail_wg = (int)(r.tails.size() / 8);
+  r.num_tiles = r.num_tail_wg + num_groups;
   r.kt_pad = r.poffs[r.P];
   r.slot_rows = (int)align_up(max_n, dita::kSlotRowAlign);
   *out = std::move(r);
@@ -242,7 +267,8 @@ struct Layout {
 Layout compute_layout(const Geo& g, int num_slots) {
   Layout L;
   const size_t P = g.P;
-  const size_t words = dita::kPlanHeader + 2 * (P + 1) + g.num_tiles + 4 * P + 2 * P * P;
+  const size_t words =
+      dita::kPlanHeader + 2 * (P + 1) + g.num_tiles + 8 * g.num_tail_wg + 4 * P + 2 * P * P;
   L.counters = 0;
   L.plans = 256;
   L.plan_bytes = align_up(words * 4, 256);
@@ -354,15 +380,15 @@ void encode_plan(const dita_cache* c, const std::vector<uint8_t>& M, int32_t* w)
   int at = dita::kPlanHeader;
   w[0] = g.num_tiles;
   w[1] = P;
-  w[3] = 0;
+  w[3] = g.num_tail_wg;
   for (int p = 0; p <= P; ++p) w[at + p] = g.offs[p];
   at += P + 1;
   for (int p = 0; p <= P; ++p) w[at + p] = g.poffs[p];
   at += P + 1;
-  for (int i = 0; i < P; ++i) {
-    const int n = g.offs[i + 1] - g.offs[i];
-    for (int t = 0; t * g.wg_rows < n; ++t) w[at++] = (i << 16) | t;
-  }
+  for (int k = 0; k < g.num_tail_wg; ++k) w[at++] = dita::kTailFlag | k;
+  for (int i = 0; i < P; ++i)
+    for (int t = 0; t < g.groups[i]; ++t) w[at++] = (i << 16) | t;
+  for (int32_t v : g.tails) w[at++] = v;
   const int rows_at = at;
   int ent_at = rows_at + 4 * P;
   int e = 0;
@@ -395,7 +421,8 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->off_offs = dita::kPlanHeader;
   a->off_poffs = a->off_offs + P + 1;
   a->off_tiles = a->off_poffs + P + 1;
-  a->off_rows = a->off_tiles + g.num_tiles;
+  a->off_tail = a->off_tiles + g.num_tiles;
+  a->off_rows = a->off_tail + 8 * g.num_tail_wg;
   a->off_ent = a->off_rows + 4 * P;
   a->B = g.B; a->H = g.H; a->N = g.N; a->D = g.D; a->DP = g.DP; a->P = P;
   a->num_tiles = g.num_tiles;

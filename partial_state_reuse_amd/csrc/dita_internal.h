@@ -28,14 +28,23 @@ inline int bf16_padded_dim(int D) {
 inline int bf16_wg_rows(int /*DP*/) { return kWaves * 32; }
 
 // Layout of one device plan (int32 words), as written by the host and read by the kernels:
-//   [0] num_tiles  [1] P  [2] E (entries)  [3] unused
+//   [0] num_tiles  [1] P  [2] E (entries)  [3] number of tail workgroups
 //   offs   at kPlanHeader                 : P+1 partition offsets o_p
 //   poffs  at kPlanHeader + (P+1)         : P+1 padded offsets of the transposed-V scratch
-//   tiles  at kPlanHeader + 2(P+1)        : num_tiles words, (i << 16) | tile-in-partition
-//   rows   at tiles + num_tiles           : P x 4 words {first entry, #fresh, #reuse, 0}
+//   tiles  at kPlanHeader + 2(P+1)        : num_tiles words: (i << 16) | group-in-partition
+//                                           for a workgroup of 4 waves on consecutive rows,
+//                                           or kTailFlag | k for tail workgroup k
+//   tails  at tiles + num_tiles           : 8 words per tail workgroup: {i, first row} of the
+//                                           32-row sub-tile each of its 4 waves owns ({-1, 0}:
+//                                           none)
+//   rows   at tails + 8 * tail workgroups : P x 4 words {first entry, #fresh, #reuse, 0}
 //   ent    at rows + 4P                   : E x 2 words {j, slot}; per row the fresh blocks
 //                                           (ascending j) precede the reused ones
 constexpr int kPlanHeader = 4;
+constexpr int32_t kTailFlag = 1 << 30;
+// bf16 path: a partition whose last row group would leave at most this many of its 4 waves
+// with rows hands those rows to tail workgroups instead (sub-tiles packed 4 per workgroup).
+constexpr int kMaxTailSubtiles = 2;
 
 struct StepArgs {
   const void* q;
@@ -50,7 +59,7 @@ struct StepArgs {
   unsigned long long* counters;  // [0] fresh blocks, [1] reused blocks, [2] V elements
                                  // outside the fp16 range (cumulative)
   const int32_t* plan;       // device plan (layout above)
-  int32_t off_offs, off_poffs, off_tiles, off_rows, off_ent;
+  int32_t off_offs, off_poffs, off_tiles, off_tail, off_rows, off_ent;
   int32_t B, H, N, D, DP, P;
   int32_t num_tiles;         // workgroup tiles per (b, h)
   int32_t num_slots;

@@ -157,13 +157,236 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 fused step.  Workgroup = 4 waves = 128 query rows of one partition; each wave owns a
-// 32-row sub-tile (lane l: query row l%32).
+// bf16 fused step.  Each wave owns a 32-row sub-tile of one query partition (lane l: query
+// row l%32).  Two kinds of workgroup, 4 waves each:
+//   group: the 4 waves take 128 consecutive rows of one partition and share every K / V^T
+//          tile, staged in LDS;
+//   tail:  4 independent sub-tiles (left over at the ends of partitions, possibly of
+//          different partitions); each wave reads its K / V^T fragments straight from
+//          global memory, with no LDS and no barrier.
 // ------------------------------------------------------------------------------------------
 // Lazy rescale: the running reference m of a block state is raised only when a new logit
 // exceeds it by more than this many powers of two, so p = 2^(s - m) stays <= 2^8 and the
 // accumulator is rescaled rarely (the result is exact either way: m is only a reference).
 constexpr float kRescaleSlack = 8.0f;
+
+// Block end, for the wave's 32-row sub-tile: normalise the block state, store it to its
+// slot (O^T fragment as bf16 in fragment order, lse as f32 natural log) and fold it into
+// the row's running merge (base-2 units).
+template <int NDT>
+__device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT], float m_b,
+                                          float l_b, int paddr, size_t slot_base, int row0,
+                                          int myrow, uint16_t* dst, f32x16 (&acc)[NDT],
+                                          float& m_row, float& l_row) {
+  const int lane = threadIdx.x & 63, h32 = lane >> 5;
+  const float lsum = sum_halves(l_b, paddr);
+  const float inv = 1.0f / lsum;
+  const float lse2 = m_b + fast_log2(lsum);      // block lse, base 2
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    bacc[dt] *= inv;
+    u32x4 w0, w1;
+    uint16_t* e0p = (uint16_t*)&w0;
+    uint16_t* e1p = (uint16_t*)&w1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      e0p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][r]);
+      e1p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][r + 8]);
+    }
+    st16(dst + dt * 1024 + lane * 16, w0);
+    st16(dst + dt * 1024 + lane * 16 + 8, w1);
+  }
+  if (h32 == 0) a.cache_lse[slot_base * a.slot_rows + myrow] = lse2 * kLn2;
+  const float mn = fmaxf(m_row, lse2);
+  const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * fa + bacc[dt] * fb;
+  l_row = l_row * fa + fb;
+  m_row = mn;
+}
+
+// Reused blocks folded into the row's merge, then the epilogue (out = acc / l, lse) and the
+// per-partition block counts, for the wave's 32-row sub-tile.
+template <int DP>
+__device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int i, int o_i,
+                                                 int n_i, int row0, int e0, int nf, int nr,
+                                                 f32x16 (&acc)[DP / 32], float m_row,
+                                                 float l_row) {
+  constexpr int NDT = DP / 32;
+  const int lane = threadIdx.x & 63, h32 = lane >> 5, l32 = lane & 31;
+  const int myrow = row0 + l32;
+  const cint* ent = as_const(a.plan) + a.off_ent;
+  const size_t slot_elems = (size_t)a.slot_rows * DP;
+  const uint16_t* cache_o = (const uint16_t*)a.cache_o;
+  for (int e = nf; e < nf + nr; ++e) {
+    const int slot = ent[2 * (e0 + e) + 1];
+    const size_t slot_base = (size_t)bh * a.num_slots + slot;
+    const float lse2 = a.cache_lse[slot_base * a.slot_rows + myrow] * kLog2e;
+    const uint16_t* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
+    u32x4 raw[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      raw[dt][0] = ld16(src + dt * 1024 + lane * 16);
+      raw[dt][1] = ld16(src + dt * 1024 + lane * 16 + 8);
+    }
+    const float mn = fmaxf(m_row, lse2);
+    const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x8 lo = as_bf16x8(raw[dt][0]), hi = as_bf16x8(raw[dt][1]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        acc[dt][r] = acc[dt][r] * fa + (float)lo[r] * fb;
+        acc[dt][r + 8] = acc[dt][r + 8] * fa + (float)hi[r] * fb;
+      }
+    }
+    l_row = l_row * fa + fb;
+    m_row = mn;
+  }
+  const size_t bhN = (size_t)bh * a.N;
+  if (myrow < n_i) {
+    const float inv = 1.0f / l_row;
+    float* orow = a.out + (bhN + o_i + myrow) * a.D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = dt * 32 + 8 * q4 + 4 * h32;
+        if (d < a.D) {
+          f32x4 v = {acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
+                     acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv};
+          *(f32x4*)(orow + d) = v;
+        }
+      }
+    }
+    if (a.lse_out && h32 == 0)
+      a.lse_out[bhN + o_i + myrow] = (m_row + fast_log2(l_row)) * kLn2;
+  }
+  // block counts, once per partition row: by the wave that holds its first rows
+  if (row0 == 0 && lane == 0) {
+    atomicAdd(&a.counters[0], (unsigned long long)nf);
+    atomicAdd(&a.counters[1], (unsigned long long)nr);
+  }
+}
+
+// Tail workgroup: 4 independent waves, each with its own 32-row sub-tile (possibly of
+// different partitions); each reads its K / V^T fragments straight from global memory (L2),
+// with no LDS and no barrier.
+template <int DP>
+__device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
+  constexpr int NKC = DP / 16, NDT = DP / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h32 = lane >> 5, l32 = lane & 31;
+  const cint* plan = as_const(a.plan);
+  const cint* offs = plan + a.off_offs;
+  const cint* poffs = plan + a.off_poffs;
+  const cint* te = plan + a.off_tail + 8 * k + 2 * wave;
+  const int i = te[0], row0 = te[1];
+  if (i < 0) return;                              // no sub-tile for this wave
+  const int o_i = offs[i], n_i = offs[i + 1] - o_i;
+  const int myrow = row0 + l32;
+  const cint* rinfo = plan + a.off_rows + 4 * i;
+  const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
+  const cint* ent = plan + a.off_ent;
+  const size_t bhN = (size_t)bh * a.N;
+  const float sc = a.scale_log2;
+  const int paddr = partner_addr();
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+  bf16x8 qf[NKC];
+  {
+    const uint16_t* Q = (const uint16_t*)a.q + bhN * a.D;
+    const bool ok = myrow < n_i;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int d0 = kc * 16 + h32 * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok && d0 < a.D) v = ld16(Q + (size_t)(o_i + myrow) * a.D + d0);
+      qf[kc] = as_bf16x8(v);
+    }
+  }
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x16){};
+  float m_row = kNegInf, l_row = 0.f;
+  const size_t slot_elems = (size_t)a.slot_rows * DP;
+  uint16_t* cache_o = (uint16_t*)a.cache_o;
+  const uint16_t* Kg = (const uint16_t*)a.k + bhN * a.D;
+  const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
+
+  // ---------------- fresh blocks ----------------
+  for (int e = 0; e < nf; ++e) {
+    const int j = ent[2 * (e0 + e)], slot = ent[2 * (e0 + e) + 1];
+    const int o_j = offs[j], n_j = offs[j + 1] - o_j, po_j = poffs[j];
+    f32x16 bacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) bacc[dt] = (f32x16){};
+    float m_b = kNegInf, l_b = 0.f;
+    for (int kbase = 0; kbase < n_j; kbase += 32) {
+      // K fragments: row key_of_row(l32) of the unit (clamped into the block: keys past its
+      // end are masked below), dims kc*16 + 8*h32 (clamped below D, where Q is zero)
+      bf16x8 kf[NKC];
+      {
+        const int key = min(kbase + key_of_row(l32), n_j - 1);
+        const uint16_t* src = Kg + (size_t)(o_j + key) * a.D;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) kf[kc] = as_bf16x8(ld16(src + min(kc * 16 + h32 * 8, a.D - 8)));
+      }
+      f32x16 s = (f32x16){};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], s, 0, 0, 0);
+      // V^T fragments: rows dt*32 + l32, keys c*16 + 8*h32 of the unit (the scratch is zero
+      // padded to whole 64-key tiles per partition, so these stay in bounds); requested
+      // after the K fragments are consumed, in flight during the softmax
+      f16x8 vf[NDT][2];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          vf[dt][c] = as_f16x8(ld16(VTg + (size_t)(dt * 32 + l32) * a.kt_pad + po_j + kbase + c * 16 + h32 * 8));
+      if (kbase + 32 > n_j) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + 16 * (r >> 3) + 8 * h32 + (r & 7);
+          if (key >= n_j) s[r] = kNegInf;
+        }
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+      for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1 < 16 ? r + 1 : r]);
+      mx = max_halves(mx, paddr) * sc;
+      if (__any(mx > m_b + kRescaleSlack)) {
+        const float m_new = fmaxf(m_b, mx);
+        const float alpha = fast_exp2(m_b - m_new);
+        m_b = m_new;
+        l_b *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= alpha;
+      }
+      f16x8 pf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pf[r >> 3][r & 7] = (_Float16)fast_exp2(__builtin_fmaf(s[r], sc, -m_b));
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const f16x2 pair = {pf[c][2 * q2], pf[c][2 * q2 + 1]};
+          l_b = __builtin_amdgcn_fdot2(pair, ones, l_b, false);
+        }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          bacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[dt][c], pf[c], bacc[dt], 0, 0, 0);
+    }
+    block_end<NDT>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
+                   cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
+                   acc, m_row, l_row);
+  }
+  reuse_and_finish<DP>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
+}
 
 template <int DP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 3 : 1))) void step_bf16(StepArgs a) {
@@ -187,6 +410,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const cint* offs = plan + a.off_offs;
   const cint* poffs = plan + a.off_poffs;
   const int packed = plan[a.off_tiles + tix];
+  if (packed & kTailFlag) {                     // workgroup-uniform
+    tail_wave<DP>(a, bh, packed & 0xffff);
+    return;
+  }
   const int i = packed >> 16, t = packed & 0xffff;
   const int o_i = offs[i], n_i = offs[i + 1] - o_i;
   const int row0 = t * WG_ROWS + wave * 32;     // first row of this wave in partition i
@@ -324,87 +551,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     }
     if (!live) continue;
 
-    // block end: normalise, write the state to its slot, fold it into the row's merge
-    const size_t slot_base = (size_t)bh * a.num_slots + slot;
-    const float lsum = sum_halves(l_b, paddr);
-    const float inv = 1.0f / lsum;
-    const float lse2 = m_b + fast_log2(lsum);
-    uint16_t* dst = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      bacc[dt] *= inv;
-      u32x4 w0, w1;
-      uint16_t* e0p = (uint16_t*)&w0;
-      uint16_t* e1p = (uint16_t*)&w1;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        e0p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][r]);
-        e1p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][r + 8]);
-      }
-      st16(dst + dt * 1024 + lane * 16, w0);
-      st16(dst + dt * 1024 + lane * 16 + 8, w1);
-    }
-    if (h32 == 0) a.cache_lse[slot_base * a.slot_rows + myrow] = lse2 * kLn2;
-    const float mn = fmaxf(m_row, lse2);
-    const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * fa + bacc[dt] * fb;
-    l_row = l_row * fa + fb;
-    m_row = mn;
+    block_end<NDT>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
+                   cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
+                   acc, m_row, l_row);
   }
   if (!live) return;
 
-  // ---------------- reused blocks ----------------
-  for (int e = nf; e < nf + nr; ++e) {
-    const int slot = ent[2 * (e0 + e) + 1];
-    const size_t slot_base = (size_t)bh * a.num_slots + slot;
-    const float lse2 = a.cache_lse[slot_base * a.slot_rows + myrow] * kLog2e;
-    const uint16_t* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
-    u32x4 raw[NDT][2];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      raw[dt][0] = ld16(src + dt * 1024 + lane * 16);
-      raw[dt][1] = ld16(src + dt * 1024 + lane * 16 + 8);
-    }
-    const float mn = fmaxf(m_row, lse2);
-    const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x8 lo = as_bf16x8(raw[dt][0]), hi = as_bf16x8(raw[dt][1]);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        acc[dt][r] = acc[dt][r] * fa + (float)lo[r] * fb;
-        acc[dt][r + 8] = acc[dt][r + 8] * fa + (float)hi[r] * fb;
-      }
-    }
-    l_row = l_row * fa + fb;
-    m_row = mn;
-  }
-
-  // ---------------- epilogue: out = acc / l, lse = m + log2(l) ----------------
-  if (myrow < n_i) {
-    const float inv = 1.0f / l_row;
-    float* orow = a.out + (bhN + o_i + myrow) * a.D;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = dt * 32 + 8 * q4 + 4 * h32;
-        if (d < a.D) {
-          f32x4 v = {acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
-                     acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv};
-          *(f32x4*)(orow + d) = v;
-        }
-      }
-    }
-    if (a.lse_out && h32 == 0)
-      a.lse_out[bhN + o_i + myrow] = (m_row + fast_log2(l_row)) * kLn2;
-  }
-
-  if (t == 0 && tid == 0) {
-    atomicAdd(&a.counters[0], (unsigned long long)nf);
-    atomicAdd(&a.counters[1], (unsigned long long)nr);
-  }
+  reuse_and_finish<DP>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
 }
 
 // ------------------------------------------------------------------------------------------
