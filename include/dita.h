@@ -61,7 +61,8 @@ typedef enum dita_policy_kind {
   DITA_POLICY_EXPLICIT = 0,           /* mask given by the caller                            */
   DITA_POLICY_FRAME_THRESHOLD = 1,    /* FRESH iff |f_i - f_j| <= max_fresh_frame_dist       */
   DITA_POLICY_FRESH_BUDGET = 2,       /* per row R = min(floor((pct*A_i + 50)/100), A_i - 1) */
-  DITA_POLICY_CENTROID_THRESHOLD = 3  /* FRESH iff |C_i - C_j| <= max_fresh_centroid2        */
+  DITA_POLICY_CENTROID_THRESHOLD = 3, /* FRESH iff |C_i - C_j| <= max_fresh_centroid2        */
+  DITA_POLICY_PLANNER = 4             /* reuse chosen by predicted error (below)              */
 } dita_policy_kind;
 
 /* Token geometry.  Tokens are (t, y, x) flattened frame-major, row-major inside a frame:
@@ -85,16 +86,40 @@ typedef struct dita_geometry {
 /* One step's block policy (DiTango, "Anchor-Guided Selection Planner"): which blocks are
  * recomputed and which reuse a cached state.  Candidates for the budget rule are ranked by
  * (|f_i - f_j|, |C_i - C_j|, j).  Whatever the kind, the diagonal block is FRESH (the local
- * partition is always computed) and only blocks of the active set are non-SKIP. */
+ * partition is always computed) and only blocks of the active set are non-SKIP.
+ *
+ * PLANNER (DiTango, "Anchor-Guided Selection Planner": error model, anchor steps, online
+ * prediction, group strategy).  Partitions p and q share a group iff p / G == q / G.  The
+ * decision unit is a block group (I, J); its members are all FRESH or all REUSE (SKIP
+ * members stay SKIP).  With E_ij the predicted error of reusing block (i, j) this step:
+ *   E_IJ = sum of E_ij over the active members, i ascending then j ascending, in double;
+ *   A_I  = active block groups of query group I, R_I = min(floor((pct A_I + 50)/100), A_I-1);
+ *   FRESH: the diagonal group, every group with a member whose slot holds no state, every
+ *   group with E_IJ > max_error (if max_error > 0), and then the groups of largest E_IJ
+ *   (ties: smaller J first) until at least A_I - R_I groups are FRESH; the rest REUSE.
+ * On a cache, E_ij = w_ij * (Cum_i(s-1) - Cum_i(f_ij) + delta_i(s-1)) for step s since the
+ * last reset, with the block's last fresh step f_ij and quantities the library measures on
+ * the device:
+ *   w_ij      importance: mean over (b, h, rows r of partition i) of exp(lse_ij[r] - L_i[r]),
+ *             L_i[r] = log sum over active j of exp(lse_ij[r]); measured on anchor steps;
+ *   delta_i(t) growth: root mean square over (b, h, rows of i, d < D) of the change of the
+ *             cached diagonal state O_ii from step t-1 to step t (the local state, always
+ *             computed, as the proxy of remote drift); Cum_i(t) = sum of delta_i up to t.
+ * Anchor steps (every active block FRESH, w refreshed): step 1 after a reset, then every
+ * anchor_period steps (steps 1, 1 + A, 1 + 2A, ...; A = 0: only step 1), a policy with
+ * anchor = 1, and a PLANNER step that has no importance measured since the reset. */
 typedef struct dita_block_policy {
   int32_t kind;                  /* dita_policy_kind                                         */
   const uint8_t* explicit_mask;  /* host, P*P row-major, kind == EXPLICIT; copied            */
   int32_t max_fresh_frame_dist;  /* FRAME_THRESHOLD                                           */
-  int32_t reuse_percent;         /* FRESH_BUDGET, 0..100                                      */
+  int32_t reuse_percent;         /* FRESH_BUDGET and PLANNER, 0..100                          */
   int32_t max_fresh_centroid2;   /* CENTROID_THRESHOLD, in doubled-token units                */
   int32_t tile_sparse;           /* 1: active iff f_j in {f_i, 0, f_i - 1, f_i + 1}
                                     (Efficient-vDiT's tile-style sparse 3D attention)         */
   int32_t anchor;                /* 1: every active block FRESH (anchor step)                 */
+  int32_t group_size;            /* PLANNER: G >= 1 (0 is read as 1)                          */
+  int32_t anchor_period;         /* PLANNER: A >= 0                                           */
+  double max_error;              /* PLANNER: error cap, <= 0 = none                           */
 } dita_block_policy;
 
 typedef struct dita_step_stats {
@@ -131,6 +156,15 @@ const char* dita_last_error(void);
  * Errors: INVALID_ARGUMENT, SHAPE, POLICY, CACHE_MISS (REUSE where valid is zero). */
 dita_status dita_policy_mask(const dita_geometry* geom, const dita_block_policy* policy,
                              const uint8_t* valid, uint8_t* mask_out);
+
+/* The PLANNER decision from given predicted errors (host only, no cache):
+ *   error     host, P*P doubles, E_ij (read for active off-diagonal blocks only)
+ *   valid     host, P*P or NULL, as for dita_policy_mask
+ *   mask_out  host, P*P
+ * policy->kind must be PLANNER; policy->anchor = 1 gives the anchor mask.
+ * Errors: INVALID_ARGUMENT, SHAPE. */
+dita_status dita_planner_mask(const dita_geometry* geom, const dita_block_policy* policy,
+                              const double* error, const uint8_t* valid, uint8_t* mask_out);
 
 /* Partition offsets the geometry resolves to: host out[P+1]. */
 dita_status dita_partition_offsets(const dita_geometry* geom, int32_t* out);
@@ -191,6 +225,18 @@ dita_status dita_cache_read_slot(dita_cache* cache, int32_t b, int32_t h, int32_
  * stream around each of its kernels and sums their durations into dita_step_stats.
  * Enabling resets the sums.  Errors: INVALID_ARGUMENT. */
 dita_status dita_set_profiling(dita_cache* cache, int32_t enable);
+
+/* The PLANNER's measured state, after waiting for the measurements of the last step:
+ *   w          host P*P f32 or NULL: importance from the last anchor step (zeros if none)
+ *   delta      host steps*P doubles or NULL: delta_i(t) for t = 1..steps, row t-1 for step t
+ *              (0 where not measured: step 1, and steps run with another policy kind)
+ *   fresh_step host P*P int32 or NULL: step since the reset at which each block was last
+ *              FRESH (0 = never)
+ *   steps      host, out: steps since the last reset
+ * Cum_i(t) = delta_i(1) + ... + delta_i(t), summed in that order.  Pass delta = NULL to
+ * query `steps` first.  Errors: INVALID_ARGUMENT, DEVICE. */
+dita_status dita_get_planner_state(dita_cache* cache, float* w, double* delta,
+                                   int32_t* fresh_step, int32_t* steps);
 
 /* Counters and last-step work.  Synchronises the device to read the device counters. */
 dita_status dita_get_stats(const dita_cache* cache, dita_step_stats* stats);

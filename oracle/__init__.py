@@ -20,14 +20,22 @@ Pins (tests/test_oracle_pins.py): dense softmax attention from torch's SDPA (all
 masked SDPA (tile mask), brute-force scalar loops over the closed "mixed-time" form,
 split/merge-order invariance, reuse-with-no-drift no-op, merge weights summing to one,
 closed-form mask counts and printed masks (tests/golden/), linear-in-frames active count,
-head-permutation equivariance and the CFG constant-shift identity.
+head-permutation equivariance and the CFG constant-shift identity.  Planner
+(tests/test_planner_oracle.py): importance against a dense-softmax brute force and the
+uniform-attention closed form, rows summing to one, growth zero without drift and equal to a
+planted constant shift, the group decision against an exhaustive search on small cases and a
+hand-worked example, and the planner reducing to the all-fresh run when every step is an
+anchor.
 """
 from .policy import (partition_offsets, centroids2, partition_frames, active_mask,
                      policy_mask, work_lists, PolicyError, SKIP, FRESH, REUSE)
 from .attention import (block_state, merge_states, round_bf16, round_f32, run_head,
                         OracleStep)
+from .planner import (importance, growth, predicted_errors, planner_mask, run_planner,
+                      PlannerStep, PLANNER)
 
 __all__ = ["partition_offsets", "centroids2", "partition_frames", "active_mask",
            "policy_mask", "work_lists", "PolicyError", "SKIP", "FRESH", "REUSE",
            "block_state", "merge_states", "round_bf16", "round_f32", "run_head",
-           "OracleStep"]
+           "OracleStep", "importance", "growth", "predicted_errors", "planner_mask",
+           "run_planner", "PlannerStep", "PLANNER"]

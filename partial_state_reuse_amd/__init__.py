@@ -29,11 +29,13 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "SHAPE", 3: "UNSUPPORTED", 4:
 F32, BF16 = 0, 1
 SKIP, FRESH, REUSE = 0, 1, 2
 POLICY_EXPLICIT, POLICY_FRAME_THRESHOLD, POLICY_FRESH_BUDGET, POLICY_CENTROID_THRESHOLD = 0, 1, 2, 3
+POLICY_PLANNER = 4
 
 EXPORTED = ["dita_version", "dita_last_error", "dita_policy_mask", "dita_partition_offsets",
             "dita_cache_required_bytes", "dita_cache_alloc", "dita_cache_reset",
             "dita_cache_free", "dita_set_block_policy", "dita_get_block_plan",
-            "dita_attn_step", "dita_cache_read_slot", "dita_set_profiling", "dita_get_stats"]
+            "dita_attn_step", "dita_cache_read_slot", "dita_set_profiling", "dita_get_stats",
+            "dita_planner_mask", "dita_get_planner_state"]
 
 
 class DitaError(RuntimeError):
@@ -57,7 +59,8 @@ class BlockPolicy(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("explicit_mask", ctypes.POINTER(ctypes.c_uint8)),
                 ("max_fresh_frame_dist", ctypes.c_int32), ("reuse_percent", ctypes.c_int32),
                 ("max_fresh_centroid2", ctypes.c_int32), ("tile_sparse", ctypes.c_int32),
-                ("anchor", ctypes.c_int32)]
+                ("anchor", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("anchor_period", ctypes.c_int32), ("max_error", ctypes.c_double)]
 
 
 class StepStats(ctypes.Structure):
@@ -75,6 +78,8 @@ class StepStats(ctypes.Structure):
 _P = ctypes.c_void_p
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _u8p = ctypes.POINTER(ctypes.c_uint8)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
 _sig = {
     "dita_version": (ctypes.c_char_p, []),
     "dita_last_error": (ctypes.c_char_p, []),
@@ -94,6 +99,9 @@ _sig = {
                                             ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "dita_set_profiling": (ctypes.c_int, [_P, ctypes.c_int32]),
     "dita_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(StepStats)]),
+    "dita_planner_mask": (ctypes.c_int, [ctypes.POINTER(Geometry), ctypes.POINTER(BlockPolicy),
+                                         _f64p, _u8p, _u8p]),
+    "dita_get_planner_state": (ctypes.c_int, [_P, _f32p, _f64p, _i32p, _i32p]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -132,7 +140,8 @@ def make_geometry(batch, heads, tokens, head_dim, frames, grid_h, grid_w, num_pa
 
 
 def make_policy(kind=POLICY_FRAME_THRESHOLD, max_fresh_frame_dist=0, reuse_percent=0,
-                max_fresh_centroid2=0, tile_sparse=False, anchor=False, explicit_mask=None):
+                max_fresh_centroid2=0, tile_sparse=False, anchor=False, explicit_mask=None,
+                group_size=1, anchor_period=0, max_error=0.0):
     p = BlockPolicy()
     p.kind = int(kind)
     p.max_fresh_frame_dist = int(max_fresh_frame_dist)
@@ -140,6 +149,9 @@ def make_policy(kind=POLICY_FRAME_THRESHOLD, max_fresh_frame_dist=0, reuse_perce
     p.max_fresh_centroid2 = int(max_fresh_centroid2)
     p.tile_sparse = int(bool(tile_sparse))
     p.anchor = int(bool(anchor))
+    p.group_size = int(group_size)
+    p.anchor_period = int(anchor_period)
+    p.max_error = float(max_error)
     if explicit_mask is not None:
         arr, ptr = _u8(np.asarray(explicit_mask).ravel())
         p._mask_keepalive = arr
@@ -155,6 +167,19 @@ def dita_policy_mask(geom: Geometry, policy: BlockPolicy, valid=None) -> np.ndar
         varr, vptr = _u8(np.asarray(valid).ravel())
     _check(_lib.dita_policy_mask(ctypes.byref(geom), ctypes.byref(policy), vptr,
                                  out.ctypes.data_as(_u8p)))
+    return out.reshape(P, P)
+
+
+def dita_planner_mask(geom: Geometry, policy: BlockPolicy, error, valid=None) -> np.ndarray:
+    """The planner's decision from predicted errors E (P x P doubles)."""
+    P = geom.num_partitions
+    out = np.zeros(P * P, dtype=np.uint8)
+    e = np.ascontiguousarray(np.asarray(error, dtype=np.float64).ravel())
+    vptr = None
+    if valid is not None:
+        varr, vptr = _u8(np.asarray(valid).ravel())
+    _check(_lib.dita_planner_mask(ctypes.byref(geom), ctypes.byref(policy),
+                                  e.ctypes.data_as(_f64p), vptr, out.ctypes.data_as(_u8p)))
     return out.reshape(P, P)
 
 
@@ -286,6 +311,20 @@ class Cache:
     def set_profiling(self, enable: bool):
         _check(_lib.dita_set_profiling(self._h, 1 if enable else 0))
 
+    def planner_state(self) -> dict:
+        """The planner's measured state (waits for the last step's measurements)."""
+        P = self.geom.num_partitions
+        steps = ctypes.c_int32(0)
+        _check(_lib.dita_get_planner_state(self._h, None, None, None, ctypes.byref(steps)))
+        w = np.zeros(P * P, dtype=np.float32)
+        delta = np.zeros(max(steps.value, 1) * P, dtype=np.float64)
+        fs = np.zeros(P * P, dtype=np.int32)
+        _check(_lib.dita_get_planner_state(self._h, w.ctypes.data_as(_f32p),
+                                           delta.ctypes.data_as(_f64p),
+                                           fs.ctypes.data_as(_i32p), ctypes.byref(steps)))
+        return {"w": w.reshape(P, P), "delta": delta[:steps.value * P].reshape(steps.value, P),
+                "fresh_step": fs.reshape(P, P), "steps": steps.value}
+
     def stats(self) -> dict:
         s = StepStats()
         _check(_lib.dita_get_stats(self._h, ctypes.byref(s)))
@@ -307,7 +346,10 @@ def policy_from(p) -> BlockPolicy:
     return make_policy(kind=p.kind, max_fresh_frame_dist=p.max_fresh_frame_dist,
                        reuse_percent=p.reuse_percent, max_fresh_centroid2=p.max_fresh_centroid2,
                        tile_sparse=p.tile_sparse, anchor=p.anchor,
-                       explicit_mask=p.explicit_mask)
+                       explicit_mask=p.explicit_mask,
+                       group_size=getattr(p, "group_size", 1),
+                       anchor_period=getattr(p, "anchor_period", 0),
+                       max_error=getattr(p, "max_error", 0.0))
 
 
 def geometry_from(cfg, offsets=None) -> Geometry:

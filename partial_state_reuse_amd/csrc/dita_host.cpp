@@ -158,6 +158,96 @@ bool tile_active(const Geo& g, int i, int j) {
   return fj == fi || fj == 0 || fj == fi - 1 || fj == fi + 1;
 }
 
+// Checks shared by every policy: diagonal FRESH, non-SKIP blocks own a slot, REUSE blocks
+// hold a state.
+dita_status validate_mask(const Geo& g, std::vector<uint8_t> M, const uint8_t* valid,
+                          const int32_t* slot_of, std::vector<uint8_t>* out) {
+  const int P = g.P;
+  for (int i = 0; i < P; ++i)
+    if (M[(size_t)i * P + i] != DITA_FRESH)
+      return fail(DITA_ERR_POLICY, "diagonal block (%d,%d) must be FRESH", i, i);
+  for (size_t b = 0; b < M.size(); ++b) {
+    if (M[b] == DITA_SKIP) continue;
+    if (slot_of && slot_of[b] < 0)
+      return fail(DITA_ERR_POLICY, "block (%d,%d) has no cache slot (not in the active mask)",
+                  (int)(b / P), (int)(b % P));
+    if (M[b] == DITA_REUSE && (!valid || !valid[b]))
+      return fail(DITA_ERR_CACHE_MISS, "block (%d,%d) is REUSE but its slot holds no state",
+                  (int)(b / P), (int)(b % P));
+  }
+  *out = std::move(M);
+  return ok();
+}
+
+// PLANNER decision (DiTango, "Anchor-Guided Selection Planner": error model and group
+// strategy).  E (P*P, may be null when anchor) holds the predicted reuse errors.  Decision
+// unit: block group (I, J) of G x G partitions; its active members are all FRESH or all
+// REUSE.  Per query group: the diagonal group, groups with a member whose slot holds no
+// state, and groups whose summed error exceeds max_error (if > 0) are FRESH; then groups of
+// largest summed error (ties: smaller J) until A - R are FRESH, R = min(floor((pct A + 50) /
+// 100), A - 1) of the A active groups.  Sums run in double, i ascending then j ascending.
+dita_status planner_decide(const Geo& g, const dita_block_policy* pol, const double* E,
+                           const uint8_t* valid, const int32_t* slot_of, bool anchor,
+                           std::vector<uint8_t>* out) {
+  const int P = g.P;
+  if (pol->reuse_percent < 0 || pol->reuse_percent > 100)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "reuse_percent must be in 0..100");
+  if (pol->group_size < 0 || pol->anchor_period < 0)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "group_size and anchor_period must be >= 0");
+  if (!anchor && !E) return fail(DITA_ERR_INVALID_ARGUMENT, "error is NULL");
+  const int G = pol->group_size > 0 ? pol->group_size : 1;
+  const int NG = (P + G - 1) / G;
+  auto active = [&](int i, int j) { return !pol->tile_sparse || tile_active(g, i, j); };
+  std::vector<uint8_t> M((size_t)P * P, DITA_SKIP);
+  struct Cand { int J; double e; bool forced; };
+  std::vector<Cand> cand;
+  for (int I = 0; I < NG; ++I) {
+    const int i0 = I * G, i1 = std::min(P, i0 + G);
+    cand.clear();
+    for (int J = 0; J < NG; ++J) {
+      const int j0 = J * G, j1 = std::min(P, j0 + G);
+      bool any = false, invalid = false;
+      double e = 0.0;
+      for (int i = i0; i < i1; ++i)
+        for (int j = j0; j < j1; ++j) {
+          if (!active(i, j)) continue;
+          any = true;
+          const size_t b = (size_t)i * P + j;
+          if (!valid || !valid[b]) invalid = true;
+          if (!anchor && i != j) e += E[b];
+        }
+      if (any) cand.push_back({J, e, anchor || J == I || invalid ||
+                                         (pol->max_error > 0.0 && e > pol->max_error)});
+    }
+    const int A = (int)cand.size();
+    const int n_reuse = std::min((pol->reuse_percent * A + 50) / 100, A - 1);
+    int n_fresh = 0;
+    for (const Cand& c : cand) n_fresh += c.forced;
+    std::vector<const Cand*> rest;
+    for (const Cand& c : cand)
+      if (!c.forced) rest.push_back(&c);
+    std::sort(rest.begin(), rest.end(), [](const Cand* a, const Cand* b) {
+      if (a->e != b->e) return a->e > b->e;
+      return a->J < b->J;
+    });
+    std::vector<uint8_t> gfresh(NG, 0);
+    for (const Cand& c : cand)
+      if (c.forced) gfresh[c.J] = 1;
+    for (const Cand* c : rest)
+      if (n_fresh < A - n_reuse) {
+        gfresh[c->J] = 1;
+        ++n_fresh;
+      }
+    for (const Cand& c : cand) {
+      const int j0 = c.J * G, j1 = std::min(P, j0 + G);
+      for (int i = i0; i < i1; ++i)
+        for (int j = j0; j < j1; ++j)
+          if (active(i, j)) M[(size_t)i * P + j] = gfresh[c.J] ? DITA_FRESH : DITA_REUSE;
+    }
+  }
+  return validate_mask(g, std::move(M), valid, slot_of, out);
+}
+
 // Mask of one step.  `valid` (P*P, may be null) marks slots holding an earlier state;
 // `slot_of` (P*P, may be null) marks blocks that own a cache slot (>= 0).
 dita_status eval_policy(const Geo& g, const dita_block_policy* pol, const uint8_t* valid,
@@ -216,26 +306,20 @@ dita_status eval_policy(const Geo& g, const dita_block_policy* pol, const uint8_
       }
       row[i] = DITA_FRESH;   // the local partition is always computed
     }
+  } else if (pol->kind == DITA_POLICY_PLANNER) {
+    if (!pol->anchor)
+      return fail(DITA_ERR_INVALID_ARGUMENT,
+                  "a PLANNER step needs predicted errors: use a cache or dita_planner_mask");
+    return planner_decide(g, pol, nullptr, valid, slot_of, true, out);
   } else {
     return fail(DITA_ERR_INVALID_ARGUMENT, "unknown policy kind %d", pol->kind);
   }
-  for (int i = 0; i < P; ++i)
-    if (M[(size_t)i * P + i] != DITA_FRESH)
-      return fail(DITA_ERR_POLICY, "diagonal block (%d,%d) must be FRESH", i, i);
-  for (size_t b = 0; b < M.size(); ++b) {
-    if (M[b] == DITA_SKIP) continue;
-    if (slot_of && slot_of[b] < 0)
-      return fail(DITA_ERR_POLICY, "block (%d,%d) has no cache slot (not in the active mask)",
-                  (int)(b / P), (int)(b % P));
-    if (M[b] == DITA_REUSE && (!valid || !valid[b]))
-      return fail(DITA_ERR_CACHE_MISS, "block (%d,%d) is REUSE but its slot holds no state",
-                  (int)(b / P), (int)(b % P));
-  }
-  *out = std::move(M);
-  return ok();
+  return validate_mask(g, std::move(M), valid, slot_of, out);
 }
 
 struct Plan {
+  bool planner_w = false;        // measure the importance after the step (anchor)
+  bool planner_delta = false;    // measure the diagonal states' change during the step
   std::vector<uint8_t> mask;
   std::vector<int32_t> fresh_ptr, fresh_cols, reuse_ptr, reuse_cols;
   std::array<int32_t, 3> counts{};
@@ -261,7 +345,8 @@ void build_lists(int P, const std::vector<uint8_t>& M, Plan* p) {
 }
 
 struct Layout {
-  size_t counters = 0, plans = 0, plan_bytes = 0, vt = 0, lse = 0, o = 0, total = 0;
+  size_t counters = 0, plans = 0, plan_bytes = 0, vt = 0, lse = 0, o = 0, delta = 0, pout = 0,
+         total = 0;
 };
 
 Layout compute_layout(const Geo& g, int num_slots) {
@@ -281,6 +366,12 @@ Layout compute_layout(const Geo& g, int num_slots) {
   L.o = at;
   const size_t esz = g.cache_o == DITA_BF16 ? 2 : 4;
   at = align_up(at + bh * num_slots * (size_t)g.slot_rows * g.DP * esz, 256);
+  // planner measurement: per (b, h, i, 32-row sub-tile) squared changes, then the reduced
+  // importance (P*P f32) and growth (P f32)
+  L.delta = at;
+  at = align_up(at + bh * P * (size_t)(g.slot_rows / 32) * 4, 256);
+  L.pout = at;
+  at = align_up(at + (P * P + P) * 4, 256);
   L.total = at;
   return L;
 }
@@ -346,6 +437,17 @@ struct dita_cache {
   int timing_next = 0;
   uint64_t profiled_steps = 0;
   double step_ms = 0, prep_ms = 0;
+  // planner state since the last reset
+  int32_t steps_since_reset = 0;
+  std::vector<int32_t> fresh_step;   // P*P step since reset of the last FRESH (0 = never)
+  std::vector<float> w;              // P*P importance of the last anchor
+  bool have_w = false;
+  std::vector<double> delta_hist;    // steps_since_reset * P: delta_i(t) (0: not measured)
+  // planner measurement in flight (device -> pinned host)
+  float* meas_host = nullptr;        // pinned: P*P importance, then P growth
+  hipEvent_t meas_event = nullptr;
+  bool meas_pending = false, meas_w = false, meas_delta = false, meas_discard = false;
+  int32_t meas_step = 0;
 };
 
 namespace {
@@ -430,6 +532,8 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->slot_rows = g.slot_rows;
   a->kt_pad = g.kt_pad;
   a->scale_log2 = g.tau * 1.4426950408889634f;
+  a->delta_part = nullptr;
+  a->delta_stride = g.slot_rows / 32;
 }
 
 dita_status hip_check(hipError_t e, const char* what) {
@@ -522,6 +626,46 @@ dita_status acquire_plan(dita_cache* c, const std::vector<uint8_t>& M, hipStream
   return ok();
 }
 
+// Fold the planner measurement of an earlier step into the host state (waits for it).
+dita_status planner_sync(dita_cache* c) {
+  if (!c->meas_pending) return ok();
+  dita_status st = hip_check(hipEventSynchronize(c->meas_event), "hipEventSynchronize");
+  if (st) return st;
+  const int P = c->g.P;
+  if (!c->meas_discard) {
+    if (c->meas_delta)
+      for (int i = 0; i < P; ++i)
+        c->delta_hist[(size_t)(c->meas_step - 1) * P + i] = (double)c->meas_host[(size_t)P * P + i];
+    if (c->meas_w) {
+      c->w.assign(c->meas_host, c->meas_host + (size_t)P * P);
+      c->have_w = true;
+    }
+  }
+  c->meas_pending = c->meas_discard = false;
+  return ok();
+}
+
+// Predicted reuse errors of step s (since the reset): E_ij = w_ij * (Cum_i(s-1) - Cum_i(f_ij)
+// + delta_i(s-1)), Cum summed in step order, for blocks with a state; 0 elsewhere.
+void planner_errors(const dita_cache* c, int s, std::vector<double>* E) {
+  const int P = c->g.P;
+  std::vector<double> cum((size_t)s * P, 0.0);   // cum[t * P + i] = Cum_i(t), t = 0..s-1
+  for (int t = 1; t < s; ++t)
+    for (int i = 0; i < P; ++i)
+      cum[(size_t)t * P + i] = cum[(size_t)(t - 1) * P + i] + c->delta_hist[(size_t)(t - 1) * P + i];
+  E->assign((size_t)P * P, 0.0);
+  for (int i = 0; i < P; ++i) {
+    const double last = c->delta_hist[(size_t)(s - 2) * P + i];
+    for (int j = 0; j < P; ++j) {
+      const size_t b = (size_t)i * P + j;
+      const int f = c->fresh_step[b];
+      if (!c->valid[b] || f <= 0) continue;
+      const double drift = (cum[(size_t)(s - 1) * P + i] - cum[(size_t)f * P + i]) + last;
+      (*E)[b] = (double)c->w[b] * drift;
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -593,6 +737,8 @@ dita_status dita_cache_alloc(const dita_geometry* geom, const uint8_t* active_ma
   c->dev_bytes = buffer_bytes;
   c->valid.assign((size_t)c->g.P * c->g.P, 0);
   c->last_fresh.assign((size_t)c->g.P * c->g.P, 0);
+  c->fresh_step.assign((size_t)c->g.P * c->g.P, 0);
+  c->w.assign((size_t)c->g.P * c->g.P, 0.f);
   *out = c;
   return ok();
 }
@@ -602,6 +748,12 @@ dita_status dita_cache_reset(dita_cache* c) {
   std::fill(c->valid.begin(), c->valid.end(), 0);
   std::fill(c->last_fresh.begin(), c->last_fresh.end(), 0);
   c->has_pending = false;
+  c->steps_since_reset = 0;
+  std::fill(c->fresh_step.begin(), c->fresh_step.end(), 0);
+  std::fill(c->w.begin(), c->w.end(), 0.f);
+  c->have_w = false;
+  c->delta_hist.clear();
+  if (c->meas_pending) c->meas_discard = true;   // its copy may still be in flight
   return ok();
 }
 
@@ -619,16 +771,42 @@ dita_status dita_cache_free(dita_cache* c) {
     }
     if (c->staging) (void)hipHostFree(c->staging);
   }
+  if (c->meas_event) {
+    (void)hipEventSynchronize(c->meas_event);
+    (void)hipEventDestroy(c->meas_event);
+  }
+  if (c->meas_host) (void)hipHostFree(c->meas_host);
   delete c;
   return ok();
 }
 
 dita_status dita_set_block_policy(dita_cache* c, const dita_block_policy* policy) {
   if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!policy) return fail(DITA_ERR_INVALID_ARGUMENT, "policy is NULL");
   std::vector<uint8_t> M;
-  dita_status st = eval_policy(c->g, policy, c->valid.data(), c->slot_of.data(), &M);
-  if (st) return st;
+  bool meas_w = false, meas_delta = false;
+  if (policy->kind == DITA_POLICY_PLANNER) {
+    // DiTango planner: the previous step's measurements decide this one (waits for them)
+    dita_status st = planner_sync(c);
+    if (st) return st;
+    const int s = c->steps_since_reset + 1;
+    const int A = policy->anchor_period;
+    const bool anchor = policy->anchor || s == 1 || !c->have_w ||
+                        (A > 0 && (s - 1) % A == 0);
+    std::vector<double> E;
+    if (!anchor) planner_errors(c, s, &E);
+    st = planner_decide(c->g, policy, anchor ? nullptr : E.data(), c->valid.data(),
+                        c->slot_of.data(), anchor, &M);
+    if (st) return st;
+    meas_w = anchor;
+    meas_delta = s >= 2;
+  } else {
+    dita_status st = eval_policy(c->g, policy, c->valid.data(), c->slot_of.data(), &M);
+    if (st) return st;
+  }
   build_lists(c->g.P, M, &c->pending);
+  c->pending.planner_w = meas_w;
+  c->pending.planner_delta = meas_delta;
   c->has_pending = true;
   return ok();
 }
@@ -667,6 +845,24 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
   dita::StepArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse_out = lse_out;
   fill_args(c, pslot, &a);
+  const bool measure = c->pending.planner_w || c->pending.planner_delta;
+  if (measure) {
+    st = planner_sync(c);   // no-op unless a measurement was never collected
+    if (st) return st;
+    if (!c->meas_host) {
+      void* hp = nullptr;
+      st = hip_check(hipHostMalloc(&hp, ((size_t)c->g.P * c->g.P + c->g.P) * 4,
+                                   hipHostMallocDefault), "hipHostMalloc");
+      if (st) return st;
+      c->meas_host = (float*)hp;
+    }
+    if (!c->meas_event) {
+      st = hip_check(hipEventCreateWithFlags(&c->meas_event, hipEventDisableTiming),
+                     "hipEventCreate");
+      if (st) return st;
+    }
+  }
+  if (c->pending.planner_delta) a.delta_part = (float*)(c->dev + c->L.delta);
   TimedStep* ts = nullptr;
   if (c->profiling) {
     ts = &c->timing[c->timing_next];
@@ -703,17 +899,45 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
     ts->two_kernels = c->g.bf16();
     c->timing_next = (c->timing_next + 1) % kTimingRing;
   }
+  if (measure) {
+    // planner reductions and their copy back, collected at the next PLANNER policy
+    float* pout = (float*)(c->dev + c->L.pout);
+    const size_t PP = (size_t)c->g.P * c->g.P;
+    if (c->pending.planner_delta) {
+      st = hip_check(dita::launch_planner_delta(a, pout + PP, s), "planner_delta launch");
+      if (st) return st;
+    }
+    if (c->pending.planner_w) {
+      st = hip_check(dita::launch_planner_weights(a, pout, s), "planner_weights launch");
+      if (st) return st;
+    }
+    st = hip_check(hipMemcpyAsync(c->meas_host, pout, (PP + c->g.P) * 4, hipMemcpyDeviceToHost,
+                                  s), "planner copy");
+    if (st) return st;
+    st = hip_check(hipEventRecord(c->meas_event, s), "hipEventRecord");
+    if (st) return st;
+  }
   st = hip_check(hipEventRecord(c->pslots[pslot].event, s), "hipEventRecord");
   if (st) return st;
   c->pslots[pslot].event_recorded = true;
   // bookkeeping (only after every enqueue succeeded)
   ++c->steps_done;
+  ++c->steps_since_reset;
   const size_t PP = (size_t)c->g.P * c->g.P;
   for (size_t b = 0; b < PP; ++b)
     if (c->pending.mask[b] == DITA_FRESH) {
       c->valid[b] = 1;
       c->last_fresh[b] = (int32_t)c->steps_done;
+      c->fresh_step[b] = c->steps_since_reset;
     }
+  c->delta_hist.resize((size_t)c->steps_since_reset * c->g.P, 0.0);
+  if (measure) {
+    c->meas_pending = true;
+    c->meas_discard = false;
+    c->meas_w = c->pending.planner_w;
+    c->meas_delta = c->pending.planner_delta;
+    c->meas_step = c->steps_since_reset;
+  }
   const uint64_t bh = (uint64_t)c->g.B * c->g.H;
   c->host_fresh += bh * (uint64_t)c->pending.counts[DITA_FRESH];
   c->host_reuse += bh * (uint64_t)c->pending.counts[DITA_REUSE];
@@ -751,6 +975,34 @@ dita_status dita_set_profiling(dita_cache* c, int32_t enable) {
     c->step_ms = c->prep_ms = 0;
   }
   c->profiling = enable != 0;
+  return ok();
+}
+
+dita_status dita_planner_mask(const dita_geometry* geom, const dita_block_policy* policy,
+                              const double* error, const uint8_t* valid, uint8_t* mask_out) {
+  if (!policy || !mask_out) return fail(DITA_ERR_INVALID_ARGUMENT, "policy and mask_out required");
+  if (policy->kind != DITA_POLICY_PLANNER)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "policy kind must be PLANNER");
+  Geo g;
+  dita_status st = resolve_geometry(geom, &g);
+  if (st) return st;
+  std::vector<uint8_t> M;
+  st = planner_decide(g, policy, policy->anchor ? nullptr : error, valid, nullptr,
+                      policy->anchor != 0, &M);
+  if (st) return st;
+  std::memcpy(mask_out, M.data(), M.size());
+  return ok();
+}
+
+dita_status dita_get_planner_state(dita_cache* c, float* w, double* delta, int32_t* fresh_step,
+                                   int32_t* steps) {
+  if (!c || !steps) return fail(DITA_ERR_INVALID_ARGUMENT, "cache and steps required");
+  dita_status st = planner_sync(c);
+  if (st) return st;
+  *steps = c->steps_since_reset;
+  if (w) std::copy(c->w.begin(), c->w.end(), w);
+  if (delta) std::copy(c->delta_hist.begin(), c->delta_hist.end(), delta);
+  if (fresh_step) std::copy(c->fresh_step.begin(), c->fresh_step.end(), fresh_step);
   return ok();
 }
 

@@ -66,12 +66,24 @@ struct StepArgs {
   int32_t slot_rows;
   int32_t kt_pad;            // padded token count of the transposed-V scratch
   float scale_log2;          // tau * log2(e)
+  // Planner measurement (null = off): at the write-back of each diagonal block the kernel
+  // stores, per 32-row sub-tile, the sum over its rows (< n_i) and dims (< D) of
+  // (new cached O - old cached O)^2 at delta_part[(bh * P + i) * delta_stride + row / 32].
+  float* delta_part;
+  int32_t delta_stride;      // slot_rows / 32
 };
 
 hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s);
 hipError_t launch_transpose_v(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t s);
+// Planner reductions, on a plan whose row lists hold every active block of each row:
+//   delta[i] = sqrt(sum over (b, h, sub-tiles of i) of delta_part / (B H n_i D))
+//   w[i P + j] = mean over (b, h, rows r of i) of exp(lse_ij[r] - L_i[r]), L_i[r] = log sum
+//                over the row's blocks of exp(lse_ij[r]) (natural log, from the cached lse)
+// Fixed summation order: the results do not depend on scheduling.
+hipError_t launch_planner_delta(const StepArgs& a, float* delta, hipStream_t s);
+hipError_t launch_planner_weights(const StepArgs& a, float* w, hipStream_t s);
 hipError_t launch_read_slot(const StepArgs& a, int bh, int slot, int i, float* o_out,
                             float* lse_out, bool bf16, hipStream_t s);
 

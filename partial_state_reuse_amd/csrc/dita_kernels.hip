@@ -170,18 +170,30 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
 // accumulator is rescaled rarely (the result is exact either way: m is only a reference).
 constexpr float kRescaleSlack = 8.0f;
 
+// Wave-wide sum (every lane gets the total), in a fixed butterfly order.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
 // Block end, for the wave's 32-row sub-tile: normalise the block state, store it to its
 // slot (O^T fragment as bf16 in fragment order, lse as f32 natural log) and fold it into
-// the row's running merge (base-2 units).
+// the row's running merge (base-2 units).  For a diagonal block with the planner measurement
+// on, the squared change of the cached O (new - old, over rows < n_i and dims < D) is summed
+// first and stored for the sub-tile.
 template <int NDT>
 __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT], float m_b,
                                           float l_b, int paddr, size_t slot_base, int row0,
                                           int myrow, uint16_t* dst, f32x16 (&acc)[NDT],
-                                          float& m_row, float& l_row) {
+                                          float& m_row, float& l_row, bool diag, int n_i,
+                                          int i, int bh) {
   const int lane = threadIdx.x & 63, h32 = lane >> 5;
   const float lsum = sum_halves(l_b, paddr);
   const float inv = 1.0f / lsum;
   const float lse2 = m_b + fast_log2(lsum);      // block lse, base 2
+  const bool measure = diag && a.delta_part != nullptr;   // wave-uniform
+  float sq = 0.f;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     bacc[dt] *= inv;
@@ -193,8 +205,23 @@ __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT]
       e0p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][r]);
       e1p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][r + 8]);
     }
+    if (measure) {
+      const u32x4 o0 = ld16(dst + dt * 1024 + lane * 16), o1 = ld16(dst + dt * 1024 + lane * 16 + 8);
+      const bf16x8 n0 = as_bf16x8(w0), n1 = as_bf16x8(w1), p0 = as_bf16x8(o0), p1 = as_bf16x8(o1);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // accumulator row r of d tile dt holds d = dt*32 + 8*(r/4) + 4*h32 + r%4
+        const int d = dt * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        const float df = r < 8 ? (float)n0[r] - (float)p0[r] : (float)n1[r - 8] - (float)p1[r - 8];
+        if (myrow < n_i && d < a.D) sq = __builtin_fmaf(df, df, sq);
+      }
+    }
     st16(dst + dt * 1024 + lane * 16, w0);
     st16(dst + dt * 1024 + lane * 16 + 8, w1);
+  }
+  if (measure) {
+    sq = wave_sum(sq);
+    if (lane == 0) a.delta_part[((size_t)bh * a.P + i) * a.delta_stride + (row0 >> 5)] = sq;
   }
   if (h32 == 0) a.cache_lse[slot_base * a.slot_rows + myrow] = lse2 * kLn2;
   const float mn = fmaxf(m_row, lse2);
@@ -383,7 +410,7 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
     }
     block_end<NDT>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
                    cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
-                   acc, m_row, l_row);
+                   acc, m_row, l_row, j == i, n_i, i, bh);
   }
   reuse_and_finish<DP>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
 }
@@ -553,7 +580,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
 
     block_end<NDT>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
                    cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
-                   acc, m_row, l_row);
+                   acc, m_row, l_row, j == i, n_i, i, bh);
   }
   if (!live) return;
 
@@ -639,6 +666,19 @@ __global__ __launch_bounds__(64) void step_f32(StepArgs a) {
     const float lse2 = m_b + fast_log2(l_b);
     const size_t base = (size_t)bh * a.num_slots + slot;
     float* dst = cache_o + base * (size_t)DP * a.slot_rows;
+    if (j == i && a.delta_part) {
+      // planner measurement: squared change of the cached diagonal state, per 32-row half
+      float sq = 0.f;
+#pragma unroll
+      for (int d = 0; d < DP; ++d) {
+        const float df = b[d] / l_b - dst[(size_t)d * a.slot_rows + r];
+        if (ok && d < D) sq = __builtin_fmaf(df, df, sq);
+      }
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+      if ((lane & 31) == 0 && t * kF32Rows + lane < n_i)
+        a.delta_part[((size_t)bh * a.P + i) * a.delta_stride + ((t * kF32Rows + lane) >> 5)] = sq;
+    }
 #pragma unroll
     for (int d = 0; d < DP; ++d) {
       b[d] = b[d] / l_b;
@@ -703,6 +743,80 @@ __global__ void read_slot(StepArgs a, int bh, int slot, int n_i, float* o_out, f
   o_out[idx] = val;
 }
 
+// ------------------------------------------------------------------------------------------
+// planner reductions (one workgroup per query partition i, fixed summation order)
+// ------------------------------------------------------------------------------------------
+// Sum of 256 per-thread doubles, tree order fixed; the result is in red[0].
+__device__ __forceinline__ void block_sum(double* red, double x) {
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+}
+
+// delta[i] = sqrt(sum of the diagonal block's squared changes / (B H n_i D))
+__global__ __launch_bounds__(256) void planner_delta(StepArgs a, float* delta) {
+  __shared__ double red[256];
+  const int i = blockIdx.x;
+  const cint* offs = as_const(a.plan) + a.off_offs;
+  const int n_i = offs[i + 1] - offs[i];
+  const int S = (n_i + 31) / 32;               // sub-tiles with rows
+  const int BH = a.B * a.H;
+  double acc = 0.0;
+  for (int k = threadIdx.x; k < BH * S; k += 256) {
+    const int bh = k / S, sub = k - bh * S;
+    acc += (double)a.delta_part[((size_t)bh * a.P + i) * a.delta_stride + sub];
+  }
+  block_sum(red, acc);
+  if (threadIdx.x == 0) delta[i] = (float)sqrt(red[0] / ((double)BH * n_i * a.D));
+}
+
+// w[i P + j] = mean over (b, h, r) of exp(lse_ij[r] - L_i[r]) for the blocks j in row i's
+// lists (an anchor plan lists every active block); 0 for the others.
+__global__ __launch_bounds__(256) void planner_weights(StepArgs a, float* w) {
+  constexpr int JB = 32;                        // blocks per pass
+  __shared__ double red[256];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const cint* plan = as_const(a.plan);
+  const cint* offs = plan + a.off_offs;
+  const int n_i = offs[i + 1] - offs[i];
+  const cint* rinfo = plan + a.off_rows + 4 * i;
+  const int e0 = rinfo[0], nb = rinfo[1] + rinfo[2];
+  const cint* ent = plan + a.off_ent;
+  const int BH = a.B * a.H;
+  const int rows = BH * n_i;
+  for (int j = tid; j < a.P; j += 256) w[(size_t)i * a.P + j] = 0.f;
+  __syncthreads();
+  for (int c0 = 0; c0 < nb; c0 += JB) {
+    double accj[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) accj[jj] = 0.0;
+    for (int q = tid; q < rows; q += 256) {
+      const int bh = q / n_i, r = q - bh * n_i;
+      const float* lrow = a.cache_lse + (size_t)bh * a.num_slots * a.slot_rows + r;
+      float mx = kNegInf;
+      for (int e = 0; e < nb; ++e) mx = fmaxf(mx, lrow[(size_t)ent[2 * (e0 + e) + 1] * a.slot_rows]);
+      float ssum = 0.f;
+      for (int e = 0; e < nb; ++e) ssum += expf(lrow[(size_t)ent[2 * (e0 + e) + 1] * a.slot_rows] - mx);
+      const float L = mx + logf(ssum);
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj)
+        if (c0 + jj < nb)
+          accj[jj] += (double)expf(lrow[(size_t)ent[2 * (e0 + c0 + jj) + 1] * a.slot_rows] - L);
+    }
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      if (c0 + jj < nb) {                       // workgroup-uniform
+        block_sum(red, accj[jj]);
+        if (tid == 0) w[(size_t)i * a.P + ent[2 * (e0 + c0 + jj)]] = (float)(red[0] / rows);
+        __syncthreads();
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s) {
@@ -730,6 +844,16 @@ hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s) {
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t s) {
   const int G = a.num_tiles * a.B * a.H;
   hipLaunchKernelGGL(step_f32, dim3(G), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_planner_delta(const StepArgs& a, float* delta, hipStream_t s) {
+  hipLaunchKernelGGL(planner_delta, dim3(a.P), dim3(256), 0, s, a, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_planner_weights(const StepArgs& a, float* w, hipStream_t s) {
+  hipLaunchKernelGGL(planner_weights, dim3(a.P), dim3(256), 0, s, a, w);
   return hipGetLastError();
 }
 

@@ -1,0 +1,113 @@
+"""GPU parity of the selection planner (DiTango, "Anchor-Guided Selection Planner"), through
+the C ABI.
+
+For every step of a planner schedule:
+  * decisions: each non-anchor mask equals the oracle's decision computed from the state the
+    library reports (importance, growth history, last fresh steps), bit for bit: floating
+    point decides an integer here, so both sides decide from the same float inputs in the
+    same float64 order;
+  * measurements: the device importance and growth against the oracle replaying the same
+    masks with the same cache rounding;
+  * outputs: against the fp64 oracle on the same masks, within the bf16 / f32 bars.
+"""
+import numpy as np
+import pytest
+
+import gpu_helpers as gh
+from gpu_helpers import compare, log
+from workloads import Policy, PLANNER, custom_config
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+# importance: lse in f32 on both sides; growth: RMS of differences of bf16-rounded states,
+# where a value near a rounding boundary can land one ulp apart on the two sides
+W_RTOL, W_ATOL = 2e-4, 1e-7
+DELTA_RTOL = {"bf16": 5e-3, "f32": 1e-4}
+
+
+@pytest.fixture(scope="module")
+def dita():
+    import partial_state_reuse_amd as d
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return d
+
+
+CASES = [
+    # name, frames, gh, gw, P, D, heads, steps, dtype, reuse %, group, anchor period, cap, tile
+    ("planner-bf16-d64", 4, 6, 10, 8, 64, 3, 7, "bf16", 60, 1, 4, 0.0, False),
+    ("planner-bf16-groups", 4, 6, 10, 8, 64, 2, 6, "bf16", 50, 2, 0, 0.0, False),
+    ("planner-bf16-cap-tile", 6, 5, 7, 6, 64, 2, 6, "bf16", 70, 1, 0, 6e-3, True),
+    ("planner-bf16-d128", 3, 8, 10, 6, 128, 2, 5, "bf16", 60, 1, 3, 0.0, False),
+    ("planner-f32", 3, 4, 8, 6, 64, 2, 6, "f32", 60, 2, 0, 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_planner_schedule(dita, case):
+    import oracle
+    from oracle.policy import active_mask, partition_offsets, FRESH, SKIP
+    name, T, gh_, gw, P, D, H, S, dt, pct, G, period, cap, tile = case
+    cfg = custom_config(name=name, idx=80, heads=H, head_dim=D, frames=T, grid_h=gh_, grid_w=gw,
+                        num_partitions=P, steps=S, qkv_dtype=dt, cache_dtype=dt)
+    pol = Policy(kind=PLANNER, reuse_percent=pct, group_size=G, anchor_period=period,
+                 max_error=cap, tile_sparse=tile)
+    heads = [(0, h) for h in range(H)]
+    offs = partition_offsets(cfg.tokens, P)
+    act = active_mask(offs, cfg.frame_tokens, tile)
+    log(f"case {name}: N={cfg.tokens} P={P} D={D} H={H} steps={S} {dt} reuse={pct}% G={G} "
+        f"period={period} cap={cap} tile={tile}")
+    dev, kept = gh.device_inputs(cfg, S, keep_heads=set(heads))
+    cache = dita.Cache(dita.geometry_from(cfg), active_mask=act.astype(np.uint8))
+    masks, outs, states = [], [], []
+    for s in range(S):
+        cache.set_policy(dita.policy_from(pol))
+        masks.append(cache.plan()["mask"].copy())
+        q, k, v = dev[s]
+        out, _ = cache.step(q, k, v)
+        outs.append(out.cpu().numpy())
+        states.append(cache.planner_state())
+    cache.free()
+
+    # decisions, bit for bit
+    n_reuse_steps = 0
+    for s in range(1, S + 1):
+        M = masks[s - 1]
+        anchor = s == 1 or (period > 0 and (s - 1) % period == 0)
+        if anchor:
+            assert np.array_equal(M, np.where(act, FRESH, SKIP)), f"step {s}: anchor mask"
+            continue
+        prev = states[s - 2]
+        valid = prev["fresh_step"] > 0
+        E = oracle.predicted_errors(prev["w"], prev["delta"], prev["fresh_step"], valid, s)
+        want = oracle.planner_mask(offs, cfg.frame_tokens, pol, E, valid, False)
+        assert np.array_equal(M, want), f"step {s}: planner decision differs"
+        n_reuse_steps += int(np.any(M == 2))
+    assert n_reuse_steps > 0
+    log(f"decisions: {S} steps equal, {n_reuse_steps} with reuse")
+
+    # measurements against the oracle replaying the same masks (same cache rounding)
+    rep = oracle.run_planner(cfg, heads, pol, masks=masks, cache_mode="emulate", inputs=kept)
+    for s in range(1, S + 1):
+        st, ref = states[s - 1], rep[s - 1]
+        if ref.w is not None:
+            err = np.abs(st["w"] - ref.w)
+            assert np.all(err <= W_ATOL + W_RTOL * np.abs(ref.w)), \
+                f"step {s}: importance max err {err.max():.3e}"
+        if s >= 2:
+            got = st["delta"][s - 1]
+            rel = np.abs(got - ref.delta) / np.maximum(ref.delta, 1e-12)
+            log(f"step {s}: growth {np.round(got, 5).tolist()} rel err max {rel.max():.2e}")
+            assert np.all(rel <= DELTA_RTOL[dt]), f"step {s}: growth rel err {rel.max():.3e}"
+
+    # outputs against the fp64 oracle on the same masks
+    ref64 = oracle.run_planner(cfg, heads, pol, masks=masks, cache_mode="fp64", inputs=kept)
+    ok = True
+    for s in range(S):
+        for (b, h) in heads:
+            o, *_ = compare(outs[s][b, h], ref64[s].out[(b, h)], dt == "bf16",
+                            f"step {s + 1} head {h} out")
+            ok &= o
+    assert ok

@@ -28,6 +28,7 @@ EXPLICIT = 0
 FRAME_THRESHOLD = 1
 FRESH_BUDGET = 2
 CENTROID_THRESHOLD = 3
+PLANNER = 4
 
 
 @dataclass(frozen=True)
@@ -41,6 +42,9 @@ class Policy:
     tile_sparse          restrict the active set to {own frame, frame 0, own frame +- 1}
     anchor               every active block is fresh this step
     explicit_mask        EXPLICIT: P*P values in {0 skip, 1 fresh, 2 reuse}, row-major
+    group_size           PLANNER: partitions per group (decisions per block group)
+    anchor_period        PLANNER: steps between anchors (0: only the first)
+    max_error            PLANNER: block groups above this predicted error are fresh (0: off)
     """
 
     kind: int = FRAME_THRESHOLD
@@ -50,13 +54,17 @@ class Policy:
     tile_sparse: bool = False
     anchor: bool = False
     explicit_mask: Optional[Tuple[int, ...]] = None
+    group_size: int = 1
+    anchor_period: int = 0
+    max_error: float = 0.0
 
     def as_anchor(self) -> "Policy":
         return Policy(kind=self.kind, max_fresh_frame_dist=self.max_fresh_frame_dist,
                       reuse_percent=self.reuse_percent,
                       max_fresh_centroid2=self.max_fresh_centroid2,
                       tile_sparse=self.tile_sparse, anchor=True,
-                      explicit_mask=self.explicit_mask)
+                      explicit_mask=self.explicit_mask, group_size=self.group_size,
+                      anchor_period=self.anchor_period, max_error=self.max_error)
 
 
 @dataclass(frozen=True)
