@@ -38,7 +38,7 @@ from workloads.gen import head_steps_packed, head_steps  # noqa: E402
 METRIC = "dense-equiv attention TFLOP/s + ms/step, % of MFMA+HBM roofline, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
-KERNEL_NAME = "step_bf16<64>"
+KERNEL_NAME = "step_bf16<64, false>"
 
 
 def _gen_job(args):
@@ -58,29 +58,17 @@ def _oracle_job(args):
         return time.perf_counter() - t0
 
 
-def schedule_work(cfg):
-    """Per schedule step: (fresh FLOPs, cache read bytes, cache write bytes), from the
-    library's own policy evaluation (host only)."""
-    import partial_state_reuse_amd as dita
-    g = dita.geometry_from(cfg)
-    offs = dita.dita_partition_offsets(g).astype(np.int64)
-    n = np.diff(offs).astype(np.float64)
-    P = cfg.num_partitions
-    valid = np.zeros((P, P), np.uint8)
-    bh = cfg.batch * cfg.heads
-    D = cfg.head_dim
-    out = []
-    for s in range(1, cfg.steps + 1):
-        M = dita.dita_policy_mask(g, dita.policy_from(cfg.policy(s)), valid)
-        F = M == dita.FRESH
-        R = M == dita.REUSE
-        flops = float(4.0 * D * (n[:, None] * n[None, :])[F].sum()) * bh
-        per_row = n * (D * 2 + 4)
-        rd = float((R * per_row[:, None]).sum()) * bh
-        wr = float((F * per_row[:, None]).sum()) * bh
-        out.append((flops, rd, wr))
-        valid |= F.astype(np.uint8)
-    return out
+def mask_work(M, n, bh, D, cache_elem=2):
+    """(fresh FLOPs, cache read bytes, cache write bytes) of one step's block mask
+    (1 = fresh, 2 = reuse): 4 n_i n_j D per fresh block, n_i (D s_c + 4) bytes per reused
+    or written block, times B*H."""
+    F = M == 1
+    R = M == 2
+    flops = float(4.0 * D * (n[:, None] * n[None, :])[F].sum()) * bh
+    per_row = n * (D * cache_elem + 4)
+    rd = float((R * per_row[:, None]).sum()) * bh
+    wr = float((F * per_row[:, None]).sum()) * bh
+    return flops, rd, wr
 
 
 def kernel_source_digest():
@@ -113,6 +101,11 @@ def main():
     ap.add_argument("--workload", type=int, default=3,
                     help="workload number (the bench line is workload 3; others for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--policy", choices=["schedule", "planner"], default="schedule",
+                    help="schedule: the workload's fixed block schedule (the bench line); "
+                         "planner: the selection planner at the same reuse budget")
+    ap.add_argument("--planner-group", type=int, default=1)
+    ap.add_argument("--planner-anchor-period", type=int, default=0)
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
@@ -158,16 +151,30 @@ def main():
     cache = dita.Cache(geom, active_mask=act.astype(np.uint8))
     out = torch.empty((B, H, N, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    policies = [dita.policy_from(cfg.policy(s)) for s in range(1, S + 1)]
-    work = schedule_work(cfg)
+    if args.policy == "planner":
+        from workloads import Policy, PLANNER
+        pct = cfg.policy(2).reuse_percent
+        pl = Policy(kind=PLANNER, reuse_percent=pct, group_size=args.planner_group,
+                    anchor_period=args.planner_anchor_period,
+                    tile_sparse=cfg.policy(1).tile_sparse)
+        policies = [dita.policy_from(pl)] * S
+        schedule_desc = (f"selection planner: step 1 anchor, then {pct} % reuse chosen by "
+                         f"predicted error (importance x growth), group size "
+                         f"{args.planner_group}, anchor period {args.planner_anchor_period}")
+    else:
+        policies = [dita.policy_from(cfg.policy(s)) for s in range(1, S + 1)]
+        schedule_desc = "step 1 anchor (all fresh), then fresh budget 13/32 per row"
+    n_part = np.diff(dita.dita_partition_offsets(geom).astype(np.int64)).astype(np.float64)
     dense_flops = 4.0 * B * H * N * N * D
     stream = torch.cuda.current_stream()
+    step_masks = []
 
     def run_step(k):
         s = k % S
         if s == 0:
             cache.reset()
         cache.set_policy(policies[s])
+        step_masks.append(cache.plan()["mask"])      # host copy of the plan, no device wait
         q, kk, v = dev[s]
         cache.step(q, kk, v, out=out, lse=lse, stream=stream)
 
@@ -203,8 +210,9 @@ def main():
     ms_per_step = wall * 1e3 / K
     value = dense_flops * K / wall / 1e12
 
-    fresh_flops = sum(work[s][0] for s in kinds)
-    cache_bytes = sum(work[s][1] + work[s][2] for s in kinds)
+    work = [mask_work(m, n_part, B * H, D, 2 if bf else 4) for m in step_masks[-K:]]
+    fresh_flops = sum(w[0] for w in work)
+    cache_bytes = sum(w[1] + w[2] for w in work)
     kern_ms = st["step_kernel_ms"]
     prep_ms = st["prep_kernel_ms"]
     launches = st["profiled_steps"]
@@ -212,10 +220,10 @@ def main():
     achieved = fresh_flops / launches / (avg_kernel_ms * 1e-3) / 1e12
     digest = kernel_source_digest()
     traffic = measured_traffic(digest)
-    t_roof_sum = sum(work[s][0] / (PEAK_BF16_TFLOPS * 1e12)
-                     + (work[s][1] + work[s][2]) / (PEAK_HBM_GBS * 1e9) for s in kinds)
-    t_roof_max = sum(max(work[s][0] / (PEAK_BF16_TFLOPS * 1e12),
-                         (work[s][1] + work[s][2]) / (PEAK_HBM_GBS * 1e9)) for s in kinds)
+    t_roof_sum = sum(w[0] / (PEAK_BF16_TFLOPS * 1e12) + (w[1] + w[2]) / (PEAK_HBM_GBS * 1e9)
+                     for w in work)
+    t_roof_max = sum(max(w[0] / (PEAK_BF16_TFLOPS * 1e12), (w[1] + w[2]) / (PEAK_HBM_GBS * 1e9))
+                     for w in work)
 
     result = {
         "metric": METRIC,
@@ -233,7 +241,7 @@ def main():
                 "0.05-sigma drift per step)",
         "config": {"workload": cfg.name, "batch": B, "heads": H, "tokens": N, "head_dim": D,
                    "partitions": cfg.num_partitions, "denoise_steps": S,
-                   "schedule": "step 1 anchor (all fresh), then fresh budget 13/32 per row",
+                   "schedule": schedule_desc,
                    "cache": "bf16 O + f32 lse", "out": "f32"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

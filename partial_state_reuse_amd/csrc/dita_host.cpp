@@ -346,7 +346,7 @@ void build_lists(int P, const std::vector<uint8_t>& M, Plan* p) {
 
 struct Layout {
   size_t counters = 0, plans = 0, plan_bytes = 0, vt = 0, lse = 0, o = 0, delta = 0, pout = 0,
-         total = 0;
+         wpart = 0, total = 0;
 };
 
 Layout compute_layout(const Geo& g, int num_slots) {
@@ -372,6 +372,8 @@ Layout compute_layout(const Geo& g, int num_slots) {
   at = align_up(at + bh * P * (size_t)(g.slot_rows / 32) * 4, 256);
   L.pout = at;
   at = align_up(at + (P * P + P) * 4, 256);
+  L.wpart = at;
+  at = align_up(at + P * (size_t)dita::planner_chunks((int)P) * P * 4, 256);
   L.total = at;
   return L;
 }
@@ -908,7 +910,8 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
       if (st) return st;
     }
     if (c->pending.planner_w) {
-      st = hip_check(dita::launch_planner_weights(a, pout, s), "planner_weights launch");
+      st = hip_check(dita::launch_planner_weights(a, pout, (float*)(c->dev + c->L.wpart), s),
+                     "planner_weights launch");
       if (st) return st;
     }
     st = hip_check(hipMemcpyAsync(c->meas_host, pout, (PP + c->g.P) * 4, hipMemcpyDeviceToHost,

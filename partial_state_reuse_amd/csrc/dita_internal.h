@@ -82,8 +82,11 @@ hipError_t launch_step_f32(const StepArgs& a, hipStream_t s);
 //   w[i P + j] = mean over (b, h, rows r of i) of exp(lse_ij[r] - L_i[r]), L_i[r] = log sum
 //                over the row's blocks of exp(lse_ij[r]) (natural log, from the cached lse)
 // Fixed summation order: the results do not depend on scheduling.
+// The importance runs as (row chunks x P) workgroups writing per-chunk sums to `part`
+// (P * planner_chunks(P) * P floats), then one sum per partition.
+inline int planner_chunks(int P) { return P >= 2048 ? 1 : (2048 / P > 64 ? 64 : 2048 / P); }
 hipError_t launch_planner_delta(const StepArgs& a, float* delta, hipStream_t s);
-hipError_t launch_planner_weights(const StepArgs& a, float* w, hipStream_t s);
+hipError_t launch_planner_weights(const StepArgs& a, float* w, float* part, hipStream_t s);
 hipError_t launch_read_slot(const StepArgs& a, int bh, int slot, int i, float* o_out,
                             float* lse_out, bool bf16, hipStream_t s);
 

@@ -182,7 +182,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // the row's running merge (base-2 units).  For a diagonal block with the planner measurement
 // on, the squared change of the cached O (new - old, over rows < n_i and dims < D) is summed
 // first and stored for the sub-tile.
-template <int NDT>
+template <int NDT, bool MEASURE>
 __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT], float m_b,
                                           float l_b, int paddr, size_t slot_base, int row0,
                                           int myrow, uint16_t* dst, f32x16 (&acc)[NDT],
@@ -192,7 +192,7 @@ __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT]
   const float lsum = sum_halves(l_b, paddr);
   const float inv = 1.0f / lsum;
   const float lse2 = m_b + fast_log2(lsum);      // block lse, base 2
-  const bool measure = diag && a.delta_part != nullptr;   // wave-uniform
+  const bool measure = MEASURE && diag;                    // wave-uniform
   float sq = 0.f;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
@@ -299,7 +299,7 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
 // Tail workgroup: 4 independent waves, each with its own 32-row sub-tile (possibly of
 // different partitions); each reads its K / V^T fragments straight from global memory (L2),
 // with no LDS and no barrier.
-template <int DP>
+template <int DP, bool MEASURE>
 __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
   constexpr int NKC = DP / 16, NDT = DP / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -408,14 +408,16 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
         for (int c = 0; c < 2; ++c)
           bacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[dt][c], pf[c], bacc[dt], 0, 0, 0);
     }
-    block_end<NDT>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
+    block_end<NDT, MEASURE>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
                    cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
                    acc, m_row, l_row, j == i, n_i, i, bh);
   }
   reuse_and_finish<DP>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
 }
 
-template <int DP>
+// MEASURE: the planner's measurement of the diagonal states' change is compiled in (a
+// separate instantiation, so that steps without it keep the leaner register allocation).
+template <int DP, bool MEASURE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 3 : 1))) void step_bf16(StepArgs a) {
   constexpr int NKC = DP / 16;        // 16-wide d chunks of Q K^T
   constexpr int NDT = DP / 32;        // 32-row d tiles of O^T
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const cint* poffs = plan + a.off_poffs;
   const int packed = plan[a.off_tiles + tix];
   if (packed & kTailFlag) {                     // workgroup-uniform
-    tail_wave<DP>(a, bh, packed & 0xffff);
+    tail_wave<DP, MEASURE>(a, bh, packed & 0xffff);
     return;
   }
   const int i = packed >> 16, t = packed & 0xffff;
@@ -578,7 +580,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     }
     if (!live) continue;
 
-    block_end<NDT>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
+    block_end<NDT, MEASURE>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
                    cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
                    acc, m_row, l_row, j == i, n_i, i, bh);
   }
@@ -773,27 +775,30 @@ __global__ __launch_bounds__(256) void planner_delta(StepArgs a, float* delta) {
   if (threadIdx.x == 0) delta[i] = (float)sqrt(red[0] / ((double)BH * n_i * a.D));
 }
 
-// w[i P + j] = mean over (b, h, r) of exp(lse_ij[r] - L_i[r]) for the blocks j in row i's
-// lists (an anchor plan lists every active block); 0 for the others.
-__global__ __launch_bounds__(256) void planner_weights(StepArgs a, float* w) {
+// Importance, stage 1: workgroup (c, i) takes chunk c of the C chunks of the (b, h, r) rows
+// of partition i and writes, for every block j of row i's lists (an anchor plan lists every
+// active block), the chunk's sum of exp(lse_ij[r] - L_i[r]) to part[(i C + c) P + j] (0 for
+// the other j).
+__global__ __launch_bounds__(256) void planner_weights_part(StepArgs a, float* part, int C) {
   constexpr int JB = 32;                        // blocks per pass
   __shared__ double red[256];
-  const int i = blockIdx.x, tid = threadIdx.x;
+  const int c = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
   const cint* plan = as_const(a.plan);
   const cint* offs = plan + a.off_offs;
   const int n_i = offs[i + 1] - offs[i];
   const cint* rinfo = plan + a.off_rows + 4 * i;
   const int e0 = rinfo[0], nb = rinfo[1] + rinfo[2];
   const cint* ent = plan + a.off_ent;
-  const int BH = a.B * a.H;
-  const int rows = BH * n_i;
-  for (int j = tid; j < a.P; j += 256) w[(size_t)i * a.P + j] = 0.f;
+  const int rows = a.B * a.H * n_i;
+  const int q0 = (int)((long long)rows * c / C), q1 = (int)((long long)rows * (c + 1) / C);
+  float* out = part + ((size_t)i * C + c) * a.P;
+  for (int j = tid; j < a.P; j += 256) out[j] = 0.f;
   __syncthreads();
   for (int c0 = 0; c0 < nb; c0 += JB) {
     double accj[JB];
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) accj[jj] = 0.0;
-    for (int q = tid; q < rows; q += 256) {
+    for (int q = q0 + tid; q < q1; q += 256) {
       const int bh = q / n_i, r = q - bh * n_i;
       const float* lrow = a.cache_lse + (size_t)bh * a.num_slots * a.slot_rows + r;
       float mx = kNegInf;
@@ -810,10 +815,23 @@ __global__ __launch_bounds__(256) void planner_weights(StepArgs a, float* w) {
     for (int jj = 0; jj < JB; ++jj) {
       if (c0 + jj < nb) {                       // workgroup-uniform
         block_sum(red, accj[jj]);
-        if (tid == 0) w[(size_t)i * a.P + ent[2 * (e0 + c0 + jj)]] = (float)(red[0] / rows);
+        if (tid == 0) out[ent[2 * (e0 + c0 + jj)]] = (float)red[0];
         __syncthreads();
       }
     }
+  }
+}
+
+// Importance, stage 2: w[i P + j] = (sum over chunks c, ascending, of part) / (B H n_i).
+__global__ __launch_bounds__(256) void planner_weights_sum(StepArgs a, const float* part, int C,
+                                                           float* w) {
+  const int i = blockIdx.x;
+  const cint* offs = as_const(a.plan) + a.off_offs;
+  const double rows = (double)a.B * a.H * (offs[i + 1] - offs[i]);
+  for (int j = threadIdx.x; j < a.P; j += 256) {
+    double t = 0.0;
+    for (int c = 0; c < C; ++c) t += (double)part[((size_t)i * C + c) * a.P + j];
+    w[(size_t)i * a.P + j] = (float)(t / rows);
   }
 }
 
@@ -832,10 +850,20 @@ hipError_t launch_transpose_v(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s) {
   const int G = a.num_tiles * a.B * a.H;
+  const bool m = a.delta_part != nullptr;
   switch (a.DP) {
-    case 64: hipLaunchKernelGGL((step_bf16<64>), dim3(G), dim3(256), 0, s, a); break;
-    case 96: hipLaunchKernelGGL((step_bf16<96>), dim3(G), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((step_bf16<128>), dim3(G), dim3(256), 0, s, a); break;
+    case 64:
+      if (m) hipLaunchKernelGGL((step_bf16<64, true>), dim3(G), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((step_bf16<64, false>), dim3(G), dim3(256), 0, s, a);
+      break;
+    case 96:
+      if (m) hipLaunchKernelGGL((step_bf16<96, true>), dim3(G), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((step_bf16<96, false>), dim3(G), dim3(256), 0, s, a);
+      break;
+    case 128:
+      if (m) hipLaunchKernelGGL((step_bf16<128, true>), dim3(G), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((step_bf16<128, false>), dim3(G), dim3(256), 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -852,8 +880,12 @@ hipError_t launch_planner_delta(const StepArgs& a, float* delta, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_planner_weights(const StepArgs& a, float* w, hipStream_t s) {
-  hipLaunchKernelGGL(planner_weights, dim3(a.P), dim3(256), 0, s, a, w);
+hipError_t launch_planner_weights(const StepArgs& a, float* w, float* part, hipStream_t s) {
+  const int C = planner_chunks(a.P);
+  hipLaunchKernelGGL(planner_weights_part, dim3(C, a.P), dim3(256), 0, s, a, part, C);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(planner_weights_sum, dim3(a.P), dim3(256), 0, s, a, part, C, w);
   return hipGetLastError();
 }
 
