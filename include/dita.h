@@ -128,7 +128,8 @@ typedef struct dita_step_stats {
   int32_t reserved;
   uint64_t device_fresh_blocks;  /* cumulative (b, h, i, j) fresh blocks counted on device   */
   uint64_t device_reuse_blocks;  /* cumulative (b, h, i, j) reused blocks counted on device  */
-  uint64_t host_fresh_blocks;    /* the same two sums from the host plans, for comparison    */
+  uint64_t host_fresh_blocks;    /* the same two sums from the host plans, for comparison
+                                    (reused: states read, a merged group counting once)       */
   uint64_t host_reuse_blocks;
   double last_fresh_flops;       /* sum over fresh blocks of 4 n_i n_j D, times B*H          */
   double last_cache_read_bytes;  /* sum over reused blocks of n_i (D*s_c + 4), times B*H     */
@@ -194,10 +195,11 @@ dita_status dita_cache_free(dita_cache* cache);
 dita_status dita_set_block_policy(dita_cache* cache, const dita_block_policy* policy);
 
 /* The plan of the pending step (or, if none is pending, of the last executed step):
- *   mask        host P*P
+ *   mask        host P*P (members of a merged group all show REUSE)
  *   fresh_ptr   host P+1; fresh_cols host >= counts[1] entries (ascending j per row)
- *   reuse_ptr   host P+1; reuse_cols host >= counts[2] entries
- *   counts      host [3]: SKIP, FRESH, REUSE
+ *   reuse_ptr   host P+1; reuse_cols host >= counts[2] entries: the states read (a merged
+ *               group appears once, as its first member)
+ *   counts      host [3]: SKIP, FRESH, REUSE blocks of the mask
  * Any output pointer may be NULL.  Errors: INVALID_ARGUMENT, NO_POLICY. */
 dita_status dita_get_block_plan(const dita_cache* cache, uint8_t* mask, int32_t* fresh_ptr,
                                 int32_t* fresh_cols, int32_t* reuse_ptr, int32_t* reuse_cols,
@@ -220,6 +222,26 @@ dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, cons
  * Errors: INVALID_ARGUMENT (indices), POLICY (block without a slot), CACHE_MISS. */
 dita_status dita_cache_read_slot(dita_cache* cache, int32_t b, int32_t h, int32_t i, int32_t j,
                                  float* o_out, float* lse_out, void* hip_stream);
+
+/* Merge cached states into coarser groups (DiTango, "State-Centric Parallel Runtime /
+ * Composizione Dinamica dei Gruppi": stored attention states are merged recursively into
+ * coarser groups, with no recomputation; exact because states compose associatively).
+ *   group     g >= 2: key partitions j and j' share a group iff j / g == j' / g
+ *   select    host, P * ceil(P/g) bytes, row-major (i, J), nonzero = merge group (i, J);
+ *             NULL = every eligible group
+ *   merged    host, out, or NULL: the number of groups merged
+ * Group (i, J) is eligible when it does not contain the diagonal block, every active member
+ * holds a state, and it covers at least two states (a member already merged into a smaller
+ * group inside J counts once: merging with g = 2 and then g = 4 gives groups of 4).  For
+ * each row r of partition i the merged state is L = log sum_s exp(lse_s[r]) and
+ * O = sum_s exp(lse_s[r] - L) O_s[r] over the group's states s, computed in f32 from the
+ * cached (rounded) states and stored, rounded to the cache precision, in the slot of the
+ * group's first active member.  From then on the group is one state: a REUSE of its members
+ * reads it once (dita_get_block_plan lists the group's first member only), and a step whose
+ * policy makes any member FRESH recomputes every member, which dissolves the group.
+ * Stream-ordered on hip_stream.  Errors: INVALID_ARGUMENT, DEVICE. */
+dita_status dita_cache_merge_groups(dita_cache* cache, int32_t group, const uint8_t* select,
+                                    int32_t* merged, void* hip_stream);
 
 /* Enable (1) or disable (0) kernel timing: the library records HIP events on the launch
  * stream around each of its kernels and sums their durations into dita_step_stats.

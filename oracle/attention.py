@@ -95,9 +95,40 @@ class OracleStep:
     block_lse: dict = field(default_factory=dict)   # (i, j) -> lse rows used this step
 
 
+def merge_groups(cache, head, P, act, group, select, rho_o, rho_l, step):
+    """Group composition (DiTango, "Composizione Dinamica dei Gruppi"): per query partition
+    i and aligned key group J of `group` partitions, merge the cached states of the group
+    into one, kept at its first active member; head[(i, j)] then names that member for every
+    member.  Eligible: J does not hold i, every active member has a state, the group covers
+    at least two states, and no state inside J also covers a block outside it.
+    Returns the number of groups merged."""
+    n = 0
+    NG = (P + group - 1) // group
+    for i in range(P):
+        for J in range(NG):
+            j0, j1 = J * group, min(P, J * group + group)
+            if j0 <= i < j1 or (select is not None and not select[i][J]):
+                continue
+            members = [j for j in range(j0, j1) if act[i, j]]
+            if not members or any((i, j) not in cache for j in members):
+                continue
+            hs = sorted({head.get((i, j), j) for j in members})
+            if len(hs) < 2 or any(not (j0 <= x < j1) for x in hs):
+                continue
+            if any(head.get((i, j), j) in hs for j in range(P) if not (j0 <= j < j1)):
+                continue
+            O, L = merge_states([cache[(i, x)][:2] for x in hs])
+            dst = members[0]
+            cache[(i, dst)] = (rho_o(O), rho_l(L), step)
+            for j in members:
+                head[(i, j)] = dst
+            n += 1
+    return n
+
+
 def run_head(cfg, b: int, h: int, steps: int | None = None, rows=None,
              cache_mode: str = "emulate", policies=None, inputs=None, offsets=None,
-             drift=None, keep_block_lse: bool = False):
+             drift=None, keep_block_lse: bool = False, merges=None, active=None):
     """Run the denoising steps of one (b, h) and return a list of OracleStep.
 
     rows        None (all tokens) or a sorted array of global token indices to evaluate;
@@ -106,6 +137,10 @@ def run_head(cfg, b: int, h: int, steps: int | None = None, rows=None,
                 and lse to float32; "fp64": no rounding.
     policies    optional list of per-step policies (default: the workload's schedule).
     inputs      optional list of per-step (Q, K, V) [N, D]; default: the seeded generator.
+    merges      optional {step: [(group, select or None), ...]}: group compositions applied
+                after that step (see merge_groups).  A merged group is then reused as one
+                state, and a step that makes any member fresh recomputes every member.
+    active      boolean [P, P] of blocks owning a cache slot (default: all).
     """
     n_steps = cfg.steps if steps is None else steps
     N, D = cfg.tokens, cfg.head_dim
@@ -129,6 +164,8 @@ def run_head(cfg, b: int, h: int, steps: int | None = None, rows=None,
         get = lambda s: inputs[s - 1]
 
     cache = {}                                   # (i, j) -> (O, lse, step)
+    head = {}                                    # (i, j) -> block holding its merged state
+    act = np.ones((P, P), dtype=bool) if active is None else np.asarray(active, dtype=bool)
     results = []
     for s in range(1, n_steps + 1):
         Qs, Ks, Vs = (np.asarray(t, dtype=np.float64) for t in get(s))
@@ -137,7 +174,26 @@ def run_head(cfg, b: int, h: int, steps: int | None = None, rows=None,
         for (i, j) in cache:
             valid[i, j] = True
         M = policy_mask(offs, cfg.frame_tokens, pol, valid)
+        # merged groups are reused or recomputed as a whole
+        covered = {k for k, v in head.items() if v != k[1]}
+        for (i, j) in covered:
+            hb = (i, head[(i, j)])
+            if M[i, j] == FRESH or M[hb] == FRESH:
+                M[i, j] = FRESH
+                M[hb] = FRESH
+        for (i, j) in covered:
+            hb = (i, head[(i, j)])
+            if M[hb] == FRESH:
+                M[i, j] = FRESH
+            if M[i, j] != M[hb]:
+                raise ValueError(f"merged block ({i},{j}) not decided with its group")
         fp, fc, rp, rc, counts = work_lists(M)
+        if covered:
+            rp, rc = [0], []
+            for i in range(P):
+                rc += [j for j in range(P) if M[i, j] == REUSE and (i, j) not in covered]
+                rp.append(len(rc))
+            rp, rc = np.array(rp, dtype=np.int32), np.array(rc, dtype=np.int32)
         out = np.zeros((len(rows), D))
         lse = np.full(len(rows), -np.inf)
         blk = {}
@@ -152,6 +208,9 @@ def run_head(cfg, b: int, h: int, steps: int | None = None, rows=None,
                     sl = slice(offs[j], offs[j + 1])
                     O_ij, l_ij = block_state(Qs[r], Ks[sl], Vs[sl], tau)
                     cache[(i, j)] = (rho_o(O_ij), rho_l(l_ij), s)
+                    head.pop((i, j), None)
+                elif (i, j) in covered:
+                    continue                     # its group's state is read once, at its head
                 else:
                     O_ij, l_ij, _ = cache[(i, j)]
                 states.append((O_ij, l_ij))
@@ -163,4 +222,6 @@ def run_head(cfg, b: int, h: int, steps: int | None = None, rows=None,
                 lse[pos:pos + len(r)] = L_i
             pos += len(r)
         results.append(OracleStep(s, M, fp, fc, rp, rc, counts, rows, out, lse, blk))
+        for (g, sel) in (merges or {}).get(s, []):
+            merge_groups(cache, head, P, act, g, sel, rho_o, rho_l, s)
     return results

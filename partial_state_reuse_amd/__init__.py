@@ -35,7 +35,7 @@ EXPORTED = ["dita_version", "dita_last_error", "dita_policy_mask", "dita_partiti
             "dita_cache_required_bytes", "dita_cache_alloc", "dita_cache_reset",
             "dita_cache_free", "dita_set_block_policy", "dita_get_block_plan",
             "dita_attn_step", "dita_cache_read_slot", "dita_set_profiling", "dita_get_stats",
-            "dita_planner_mask", "dita_get_planner_state"]
+            "dita_planner_mask", "dita_get_planner_state", "dita_cache_merge_groups"]
 
 
 class DitaError(RuntimeError):
@@ -102,6 +102,7 @@ _sig = {
     "dita_planner_mask": (ctypes.c_int, [ctypes.POINTER(Geometry), ctypes.POINTER(BlockPolicy),
                                          _f64p, _u8p, _u8p]),
     "dita_get_planner_state": (ctypes.c_int, [_P, _f32p, _f64p, _i32p, _i32p]),
+    "dita_cache_merge_groups": (ctypes.c_int, [_P, ctypes.c_int32, _u8p, _i32p, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -264,8 +265,8 @@ class Cache:
                                         fp.ctypes.data_as(_i32p), fc.ctypes.data_as(_i32p),
                                         rp.ctypes.data_as(_i32p), rc.ctypes.data_as(_i32p),
                                         counts.ctypes.data_as(_i32p)))
-        return {"mask": mask.reshape(P, P), "fresh_ptr": fp, "fresh_cols": fc[:counts[1]],
-                "reuse_ptr": rp, "reuse_cols": rc[:counts[2]], "counts": counts}
+        return {"mask": mask.reshape(P, P), "fresh_ptr": fp, "fresh_cols": fc[:fp[P]],
+                "reuse_ptr": rp, "reuse_cols": rc[:rp[P]], "counts": counts}
 
     def step(self, q, k, v, out=None, lse=None, want_lse=True, stream=None):
         """Enqueue one step on `stream` (default: torch's current stream).  q/k/v are
@@ -310,6 +311,18 @@ class Cache:
 
     def set_profiling(self, enable: bool):
         _check(_lib.dita_set_profiling(self._h, 1 if enable else 0))
+
+    def merge_groups(self, group: int, select=None, stream=None) -> int:
+        """Merge cached states of aligned groups of `group` key partitions (per query
+        partition); `select` [P, ceil(P/group)] or None for every eligible group.  Returns
+        the number of groups merged."""
+        sptr = None
+        if select is not None:
+            sarr, sptr = _u8(np.asarray(select).ravel())
+        n = ctypes.c_int32(0)
+        _check(_lib.dita_cache_merge_groups(self._h, int(group), sptr, ctypes.byref(n),
+                                            _P(_stream_handle(stream))))
+        return n.value
 
     def planner_state(self) -> dict:
         """The planner's measured state (waits for the last step's measurements)."""

@@ -321,12 +321,16 @@ struct Plan {
   bool planner_w = false;        // measure the importance after the step (anchor)
   bool planner_delta = false;    // measure the diagonal states' change during the step
   std::vector<uint8_t> mask;
+  std::vector<uint8_t> key;      // mask with covered members of merged groups marked 3
   std::vector<int32_t> fresh_ptr, fresh_cols, reuse_ptr, reuse_cols;
   std::array<int32_t, 3> counts{};
 };
 
-void build_lists(int P, const std::vector<uint8_t>& M, Plan* p) {
+// Row lists of a mask.  `covered` (P*P, may be null) marks members of merged groups whose
+// state is held by another slot: a REUSE of them reads that slot once, so they get no entry.
+void build_lists(int P, const std::vector<uint8_t>& M, const uint8_t* covered, Plan* p) {
   p->mask = M;
+  p->key = M;
   p->fresh_ptr.assign(1, 0);
   p->reuse_ptr.assign(1, 0);
   p->fresh_cols.clear();
@@ -334,10 +338,14 @@ void build_lists(int P, const std::vector<uint8_t>& M, Plan* p) {
   p->counts = {0, 0, 0};
   for (int i = 0; i < P; ++i) {
     for (int j = 0; j < P; ++j) {
-      const uint8_t m = M[(size_t)i * P + j];
+      const size_t b = (size_t)i * P + j;
+      const uint8_t m = M[b];
       p->counts[m]++;
       if (m == DITA_FRESH) p->fresh_cols.push_back(j);
-      if (m == DITA_REUSE) p->reuse_cols.push_back(j);
+      if (m == DITA_REUSE) {
+        if (covered && covered[b]) p->key[b] = 3;
+        else p->reuse_cols.push_back(j);
+      }
     }
     p->fresh_ptr.push_back((int32_t)p->fresh_cols.size());
     p->reuse_ptr.push_back((int32_t)p->reuse_cols.size());
@@ -346,7 +354,7 @@ void build_lists(int P, const std::vector<uint8_t>& M, Plan* p) {
 
 struct Layout {
   size_t counters = 0, plans = 0, plan_bytes = 0, vt = 0, lse = 0, o = 0, delta = 0, pout = 0,
-         wpart = 0, total = 0;
+         wpart = 0, merge = 0, merge_bytes = 0, total = 0;
 };
 
 Layout compute_layout(const Geo& g, int num_slots) {
@@ -374,6 +382,10 @@ Layout compute_layout(const Geo& g, int num_slots) {
   at = align_up(at + (P * P + P) * 4, 256);
   L.wpart = at;
   at = align_up(at + P * (size_t)dita::planner_chunks((int)P) * P * 4, 256);
+  // group composition jobs: at most P * ceil(P/2) jobs of 4 words, and P*P source slots
+  L.merge = at;
+  L.merge_bytes = align_up((4 * P * ((P + 1) / 2) + P * P) * 4, 256);
+  at += L.merge_bytes;
   L.total = at;
   return L;
 }
@@ -445,6 +457,12 @@ struct dita_cache {
   std::vector<float> w;              // P*P importance of the last anchor
   bool have_w = false;
   std::vector<double> delta_hist;    // steps_since_reset * P: delta_i(t) (0: not measured)
+  // group composition: head[i*P+j] = the block whose slot holds the state covering (i, j)
+  // (j itself unless (i, j) was merged into a group headed by another block)
+  std::vector<int32_t> head;
+  int32_t* merge_host = nullptr;     // pinned staging of the merge jobs (L.merge_bytes)
+  hipEvent_t merge_event = nullptr;
+  bool merge_event_recorded = false;
   // planner measurement in flight (device -> pinned host)
   float* meas_host = nullptr;        // pinned: P*P importance, then P growth
   hipEvent_t meas_event = nullptr;
@@ -467,10 +485,9 @@ void plan_work(const dita_cache* c, const Plan& p, double* flops, double* rd, do
       if (m == DITA_FRESH) {
         f += 4.0 * ni * nj * g.D;
         w += ni * (g.D * sc + 4.0);
-      } else if (m == DITA_REUSE) {
-        r += ni * (g.D * sc + 4.0);
       }
     }
+    r += (p.reuse_ptr[i + 1] - p.reuse_ptr[i]) * ni * (g.D * sc + 4.0);   // states read
   }
   *flops = f * bh;
   *rd = r * bh;
@@ -478,7 +495,7 @@ void plan_work(const dita_cache* c, const Plan& p, double* flops, double* rd, do
 }
 
 // Device plan words for a mask.
-void encode_plan(const dita_cache* c, const std::vector<uint8_t>& M, int32_t* w) {
+void encode_plan(const dita_cache* c, const Plan& pl, int32_t* w) {
   const Geo& g = c->g;
   const int P = g.P;
   int at = dita::kPlanHeader;
@@ -497,18 +514,17 @@ void encode_plan(const dita_cache* c, const std::vector<uint8_t>& M, int32_t* w)
   int ent_at = rows_at + 4 * P;
   int e = 0;
   for (int i = 0; i < P; ++i) {
-    int nf = 0, nr = 0;
     w[rows_at + 4 * i] = e;
-    for (int kind : {DITA_FRESH, DITA_REUSE})
-      for (int j = 0; j < P; ++j)
-        if (M[(size_t)i * P + j] == kind) {
-          w[ent_at + 2 * e] = j;
-          w[ent_at + 2 * e + 1] = c->slot_of[(size_t)i * P + j];
-          ++e;
-          (kind == DITA_FRESH ? nf : nr)++;
-        }
-    w[rows_at + 4 * i + 1] = nf;
-    w[rows_at + 4 * i + 2] = nr;
+    for (int x = pl.fresh_ptr[i]; x < pl.fresh_ptr[i + 1]; ++x, ++e) {
+      w[ent_at + 2 * e] = pl.fresh_cols[x];
+      w[ent_at + 2 * e + 1] = c->slot_of[(size_t)i * P + pl.fresh_cols[x]];
+    }
+    for (int x = pl.reuse_ptr[i]; x < pl.reuse_ptr[i + 1]; ++x, ++e) {
+      w[ent_at + 2 * e] = pl.reuse_cols[x];
+      w[ent_at + 2 * e + 1] = c->slot_of[(size_t)i * P + pl.reuse_cols[x]];
+    }
+    w[rows_at + 4 * i + 1] = pl.fresh_ptr[i + 1] - pl.fresh_ptr[i];
+    w[rows_at + 4 * i + 2] = pl.reuse_ptr[i + 1] - pl.reuse_ptr[i];
     w[rows_at + 4 * i + 3] = 0;
   }
   w[2] = e;
@@ -596,11 +612,10 @@ dita_status drain_all_timing(dita_cache* c) {
 }
 
 // Plan slot holding this mask on the device, uploading it if needed.
-dita_status acquire_plan(dita_cache* c, const std::vector<uint8_t>& M, hipStream_t s,
-                         int* slot) {
+dita_status acquire_plan(dita_cache* c, const Plan& pl, hipStream_t s, int* slot) {
   ++c->use_clock;
   for (int k = 0; k < dita::kPlanSlots; ++k)
-    if (c->pslots[k].used && c->pslots[k].mask == M) {
+    if (c->pslots[k].used && c->pslots[k].mask == pl.key) {
       c->pslots[k].last_use = c->use_clock;
       *slot = k;
       return ok();
@@ -616,13 +631,13 @@ dita_status acquire_plan(dita_cache* c, const std::vector<uint8_t>& M, hipStream
     if (st) return st;
   }
   int32_t* host = (int32_t*)((uint8_t*)c->staging + (size_t)victim * c->L.plan_bytes);
-  encode_plan(c, M, host);
+  encode_plan(c, pl, host);
   uint8_t* devp = c->dev + c->L.plans + (size_t)victim * c->L.plan_bytes;
   dita_status st = hip_check(
       hipMemcpyAsync(devp, host, c->L.plan_bytes, hipMemcpyHostToDevice, s), "plan upload");
   if (st) { ps.used = false; return st; }
   ps.used = true;
-  ps.mask = M;
+  ps.mask = pl.key;
   ps.last_use = c->use_clock;
   *slot = victim;
   return ok();
@@ -741,6 +756,8 @@ dita_status dita_cache_alloc(const dita_geometry* geom, const uint8_t* active_ma
   c->last_fresh.assign((size_t)c->g.P * c->g.P, 0);
   c->fresh_step.assign((size_t)c->g.P * c->g.P, 0);
   c->w.assign((size_t)c->g.P * c->g.P, 0.f);
+  c->head.resize((size_t)c->g.P * c->g.P);
+  for (size_t b = 0; b < c->head.size(); ++b) c->head[b] = (int32_t)(b % c->g.P);
   *out = c;
   return ok();
 }
@@ -756,6 +773,7 @@ dita_status dita_cache_reset(dita_cache* c) {
   c->have_w = false;
   c->delta_hist.clear();
   if (c->meas_pending) c->meas_discard = true;   // its copy may still be in flight
+  for (size_t b = 0; b < c->head.size(); ++b) c->head[b] = (int32_t)(b % c->g.P);
   return ok();
 }
 
@@ -778,6 +796,11 @@ dita_status dita_cache_free(dita_cache* c) {
     (void)hipEventDestroy(c->meas_event);
   }
   if (c->meas_host) (void)hipHostFree(c->meas_host);
+  if (c->merge_event) {
+    (void)hipEventSynchronize(c->merge_event);
+    (void)hipEventDestroy(c->merge_event);
+  }
+  if (c->merge_host) (void)hipHostFree(c->merge_host);
   delete c;
   return ok();
 }
@@ -806,7 +829,31 @@ dita_status dita_set_block_policy(dita_cache* c, const dita_block_policy* policy
     dita_status st = eval_policy(c->g, policy, c->valid.data(), c->slot_of.data(), &M);
     if (st) return st;
   }
-  build_lists(c->g.P, M, &c->pending);
+  // merged groups are reused or recomputed as a whole
+  const int P = c->g.P;
+  std::vector<uint8_t> covered((size_t)P * P, 0);
+  for (int i = 0; i < P; ++i)
+    for (int j = 0; j < P; ++j) {
+      const size_t b = (size_t)i * P + j;
+      const int h = c->head[b];
+      if (h == j) continue;
+      covered[b] = 1;
+      const size_t hb = (size_t)i * P + h;
+      if (M[b] == DITA_FRESH || M[hb] == DITA_FRESH) {
+        M[b] = DITA_FRESH;
+        M[hb] = DITA_FRESH;
+      }
+    }
+  for (int i = 0; i < P; ++i)            // a second pass spreads FRESH from a head to all
+    for (int j = 0; j < P; ++j) {
+      const size_t b = (size_t)i * P + j;
+      const size_t hb = (size_t)i * P + c->head[b];
+      if (covered[b] && M[hb] == DITA_FRESH) M[b] = DITA_FRESH;
+      if (covered[b] && M[b] != M[hb])
+        return fail(DITA_ERR_POLICY, "block (%d,%d) is merged with (%d,%d): a merged group is "
+                    "reused or recomputed as a whole", i, j, i, c->head[b]);
+    }
+  build_lists(c->g.P, M, covered.data(), &c->pending);
   c->pending.planner_w = meas_w;
   c->pending.planner_delta = meas_delta;
   c->has_pending = true;
@@ -842,7 +889,7 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
   dita_status st = device_init(c, s);
   if (st) return st;
   int pslot = 0;
-  st = acquire_plan(c, c->pending.mask, s, &pslot);
+  st = acquire_plan(c, c->pending, s, &pslot);
   if (st) return st;
   dita::StepArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse_out = lse_out;
@@ -932,6 +979,7 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
       c->valid[b] = 1;
       c->last_fresh[b] = (int32_t)c->steps_done;
       c->fresh_step[b] = c->steps_since_reset;
+      c->head[b] = (int32_t)(b % c->g.P);      // recomputed: its own state again
     }
   c->delta_hist.resize((size_t)c->steps_since_reset * c->g.P, 0.0);
   if (measure) {
@@ -943,7 +991,7 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
   }
   const uint64_t bh = (uint64_t)c->g.B * c->g.H;
   c->host_fresh += bh * (uint64_t)c->pending.counts[DITA_FRESH];
-  c->host_reuse += bh * (uint64_t)c->pending.counts[DITA_REUSE];
+  c->host_reuse += bh * (uint64_t)c->pending.reuse_cols.size();
   plan_work(c, c->pending, &c->last_flops, &c->last_rd, &c->last_wr);
   c->last = std::move(c->pending);
   c->has_last = true;
@@ -963,7 +1011,8 @@ dita_status dita_cache_read_slot(dita_cache* c, int32_t b, int32_t h, int32_t i,
   if (!c->valid[blk]) return fail(DITA_ERR_CACHE_MISS, "slot (%d,%d) holds no state", i, j);
   dita::StepArgs a{};
   fill_args(c, 0, &a);
-  return hip_check(dita::launch_read_slot(a, b * g.H + h, c->slot_of[blk],
+  const size_t hblk = (size_t)i * g.P + c->head[blk];   // a merged group's state
+  return hip_check(dita::launch_read_slot(a, b * g.H + h, c->slot_of[hblk],
                                           g.offs[i + 1] - g.offs[i], o_out, lse_out,
                                           g.bf16(), (hipStream_t)hip_stream),
                    "read_slot launch");
@@ -978,6 +1027,89 @@ dita_status dita_set_profiling(dita_cache* c, int32_t enable) {
     c->step_ms = c->prep_ms = 0;
   }
   c->profiling = enable != 0;
+  return ok();
+}
+
+dita_status dita_cache_merge_groups(dita_cache* c, int32_t group, const uint8_t* select,
+                                    int32_t* merged, void* hip_stream) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (group < 2) return fail(DITA_ERR_INVALID_ARGUMENT, "group must be >= 2");
+  if (c->has_pending)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "merge between steps, before the next policy is set");
+  const int P = c->g.P;
+  const int NG = (P + group - 1) / group;
+  std::vector<int32_t> jobs, srcs;
+  std::vector<std::pair<size_t, int32_t>> heads_new;   // (block, new head)
+  std::vector<int> members, hs;
+  for (int i = 0; i < P; ++i) {
+    const int n_i = c->g.offs[i + 1] - c->g.offs[i];
+    for (int J = 0; J < NG; ++J) {
+      const int j0 = J * group, j1 = std::min(P, j0 + group);
+      if (i >= j0 && i < j1) continue;                 // holds the always-fresh diagonal
+      if (select && !select[(size_t)i * NG + J]) continue;
+      members.clear();
+      hs.clear();
+      bool ok_group = true;
+      for (int j = j0; j < j1; ++j) {
+        const size_t b = (size_t)i * P + j;
+        if (c->slot_of[b] < 0) continue;
+        if (!c->valid[b]) { ok_group = false; break; }
+        const int h = c->head[b];
+        if (h < j0 || h >= j1) { ok_group = false; break; }   // part of a wider group
+        members.push_back(j);
+        if (std::find(hs.begin(), hs.end(), h) == hs.end()) hs.push_back(h);
+      }
+      if (!ok_group || hs.size() < 2) continue;
+      // a state inside J must not also cover blocks outside J
+      for (int j = 0; j < P && ok_group; ++j)
+        if ((j < j0 || j >= j1) &&
+            std::find(hs.begin(), hs.end(), c->head[(size_t)i * P + j]) != hs.end())
+          ok_group = false;
+      if (!ok_group) continue;
+      std::sort(hs.begin(), hs.end());
+      const int dst = members.front();                 // first active member: a head itself
+      jobs.push_back(n_i);
+      jobs.push_back(c->slot_of[(size_t)i * P + dst]);
+      jobs.push_back((int32_t)srcs.size());
+      jobs.push_back((int32_t)hs.size());
+      for (int h : hs) srcs.push_back(c->slot_of[(size_t)i * P + h]);
+      for (int j : members) heads_new.push_back({(size_t)i * P + j, dst});
+    }
+  }
+  const int njobs = (int)(jobs.size() / 4);
+  if (merged) *merged = njobs;
+  if (njobs == 0) return ok();
+  hipStream_t s = (hipStream_t)hip_stream;
+  dita_status st = device_init(c, s);
+  if (st) return st;
+  if (!c->merge_host) {
+    void* hp = nullptr;
+    st = hip_check(hipHostMalloc(&hp, c->L.merge_bytes, hipHostMallocDefault), "hipHostMalloc");
+    if (st) return st;
+    c->merge_host = (int32_t*)hp;
+    st = hip_check(hipEventCreateWithFlags(&c->merge_event, hipEventDisableTiming),
+                   "hipEventCreate");
+    if (st) return st;
+  }
+  if (c->merge_event_recorded) {                        // the staging of the previous merge
+    st = hip_check(hipEventSynchronize(c->merge_event), "hipEventSynchronize");
+    if (st) return st;
+  }
+  std::copy(jobs.begin(), jobs.end(), c->merge_host);
+  std::copy(srcs.begin(), srcs.end(), c->merge_host + jobs.size());
+  int32_t* dev = (int32_t*)(c->dev + c->L.merge);
+  st = hip_check(hipMemcpyAsync(dev, c->merge_host, (jobs.size() + srcs.size()) * 4,
+                                hipMemcpyHostToDevice, s), "merge job upload");
+  if (st) return st;
+  dita::StepArgs a{};
+  fill_args(c, 0, &a);
+  st = hip_check(dita::launch_merge_slots(a, dev, dev + jobs.size(), njobs, c->g.bf16(), s),
+                 "merge_slots launch");
+  if (st) return st;
+  st = hip_check(hipEventRecord(c->merge_event, s), "hipEventRecord");
+  if (st) return st;
+  c->merge_event_recorded = true;
+  for (const auto& hb : heads_new) c->head[hb.first] = hb.second;
   return ok();
 }
 

@@ -1,0 +1,95 @@
+"""GPU parity of group composition (DiTango, "State-Centric Parallel Runtime / Composizione
+Dinamica dei Gruppi"), through the C ABI: cached states merged into coarser groups after a
+step, then reused as one state.  Masks (with whole-group promotion) and reuse lists are
+compared bit for bit with the oracle; outputs of every step against the fp64 oracle on the
+same merges within the bf16 / f32 bars; device-counted reads against the host plan."""
+import numpy as np
+import pytest
+
+import gpu_helpers as gh
+from gpu_helpers import compare, log
+from workloads import Policy, custom_config
+from workloads import configs as wcfg
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dita():
+    import partial_state_reuse_amd as d
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return d
+
+
+CASES = [
+    # name, frames, gh, gw, P, D, heads, steps, dtype, merges {step: [(group, "sel" | None)]}
+    ("groups-bf16-d64", 8, 5, 7, 8, 64, 2, 5, "bf16", {1: [(2, "sel"), (4, "sel")]}),
+    ("groups-bf16-d128-all", 8, 4, 6, 8, 128, 1, 4, "bf16", {1: [(2, None)]}),
+    ("groups-bf16-d72-ragged", 6, 5, 7, 6, 72, 1, 4, "bf16", {1: [(3, "sel")], 2: [(6, None)]}),
+    ("groups-f32", 8, 2, 4, 8, 64, 2, 5, "f32", {2: [(2, "sel")]}),
+]
+
+
+def _always_reused(masks, P, g):
+    NG = (P + g - 1) // g
+    sel = np.ones((P, NG), bool)
+    for M in masks[1:]:
+        for i in range(P):
+            for J in range(NG):
+                if any(M[i, j] != 2 for j in range(J * g, min(P, J * g + g))):
+                    sel[i, J] = False
+    return sel
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_group_composition(dita, case):
+    import oracle
+    from oracle.policy import active_mask, partition_offsets
+    name, T, gh_, gw, P, D, H, S, dt, merges = case
+    sched = wcfg.AnchorThen(Policy(kind=wcfg.FRAME_THRESHOLD, max_fresh_frame_dist=1))
+    cfg = custom_config(name=name, idx=85, heads=H, head_dim=D, frames=T, grid_h=gh_,
+                        grid_w=gw, num_partitions=P, steps=S, qkv_dtype=dt, cache_dtype=dt,
+                        schedule=sched)
+    heads = [(0, h) for h in range(H)]
+    offs = partition_offsets(cfg.tokens, P)
+    act = active_mask(offs, cfg.frame_tokens, False)
+    base = oracle.run_head(cfg, 0, 0, cache_mode="fp64", rows=[0])   # masks only
+    resolved = {s: [(g, _always_reused([st.mask for st in base], P, g) if sel == "sel" else None)
+                    for (g, sel) in lst] for s, lst in merges.items()}
+    log(f"case {name}: N={cfg.tokens} P={P} D={D} H={H} steps={S} {dt} merges="
+        f"{ {s: [g for g, _ in l] for s, l in merges.items()} }")
+    dev, kept = gh.device_inputs(cfg, S, keep_heads=set(heads))
+    cache = dita.Cache(dita.geometry_from(cfg), active_mask=act.astype(np.uint8))
+    plans, outs, lses, n_merged = [], [], [], []
+    for s in range(1, S + 1):
+        cache.set_policy(dita.policy_from(cfg.policy(s)))
+        plans.append(cache.plan())
+        q, k, v = dev[s - 1]
+        out, lse = cache.step(q, k, v)
+        outs.append(out.cpu().numpy())
+        lses.append(lse.cpu().numpy())
+        for (g, sel) in resolved.get(s, []):
+            n_merged.append(cache.merge_groups(g, select=sel))
+    st = cache.stats()
+    cache.free()
+    assert sum(n_merged) > 0
+    assert st["device_reuse_blocks"] == st["host_reuse_blocks"]
+    log(f"groups merged: {n_merged}; states read on device {st['device_reuse_blocks']}")
+
+    ok = True
+    for (b, h) in heads:
+        ref = oracle.run_head(cfg, b, h, cache_mode="fp64", merges=resolved, active=act,
+                              inputs=kept[(b, h)])
+        for s in range(S):
+            p, r = plans[s], ref[s]
+            assert np.array_equal(p["mask"], r.mask), f"step {s + 1}: mask"
+            assert np.array_equal(p["reuse_ptr"], r.reuse_ptr), f"step {s + 1}: reuse_ptr"
+            assert np.array_equal(p["reuse_cols"], r.reuse_cols), f"step {s + 1}: reuse_cols"
+            o, *_ = compare(outs[s][b, h], r.out, dt == "bf16", f"step {s + 1} head {h} out")
+            ok &= o
+            lerr = float(np.abs(lses[s][b, h] - r.lse).max())
+            ok &= lerr < (2e-3 if dt == "bf16" else 1e-5)
+    assert ok
