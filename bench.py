@@ -58,15 +58,14 @@ def _oracle_job(args):
         return time.perf_counter() - t0
 
 
-def mask_work(M, n, bh, D, cache_elem=2):
-    """(fresh FLOPs, cache read bytes, cache write bytes) of one step's block mask
-    (1 = fresh, 2 = reuse): 4 n_i n_j D per fresh block, n_i (D s_c + 4) bytes per reused
-    or written block, times B*H."""
+def mask_work(M, reuse_ptr, n, bh, D, cache_elem=2):
+    """(fresh FLOPs, cache read bytes, cache write bytes) of one step's plan (mask: 1 = fresh,
+    2 = reuse; reuse_ptr: states read per row, a merged group counting once): 4 n_i n_j D
+    per fresh block, n_i (D s_c + 4) bytes per state read or written, times B*H."""
     F = M == 1
-    R = M == 2
     flops = float(4.0 * D * (n[:, None] * n[None, :])[F].sum()) * bh
     per_row = n * (D * cache_elem + 4)
-    rd = float((R * per_row[:, None]).sum()) * bh
+    rd = float((np.diff(reuse_ptr) * per_row).sum()) * bh
     wr = float((F * per_row[:, None]).sum()) * bh
     return flops, rd, wr
 
@@ -104,6 +103,10 @@ def main():
     ap.add_argument("--policy", choices=["schedule", "planner"], default="schedule",
                     help="schedule: the workload's fixed block schedule (the bench line); "
                          "planner: the selection planner at the same reuse budget")
+    ap.add_argument("--merge", type=str, default="",
+                    help="comma-separated group sizes (e.g. 2,4): after each run's anchor step, "
+                         "merge the cached states of every aligned key group that the schedule "
+                         "reuses on all later steps, in that order (group composition)")
     ap.add_argument("--planner-group", type=int, default=1)
     ap.add_argument("--planner-anchor-period", type=int, default=0)
     ap.add_argument("--cpu-heads", type=int, default=8)
@@ -165,6 +168,24 @@ def main():
         policies = [dita.policy_from(cfg.policy(s)) for s in range(1, S + 1)]
         schedule_desc = "step 1 anchor (all fresh), then fresh budget 13/32 per row"
     n_part = np.diff(dita.dita_partition_offsets(geom).astype(np.int64)).astype(np.float64)
+    merge_sizes = [int(x) for x in args.merge.split(",") if x]
+    merge_sel = []
+    if merge_sizes:
+        if args.policy != "schedule":
+            sys.exit("--merge applies to the fixed schedule")
+        P = cfg.num_partitions
+        later = [dita.dita_policy_mask(geom, policies[s], np.ones((P, P), np.uint8))
+                 for s in range(1, S)]
+        for g in merge_sizes:
+            NG = (P + g - 1) // g
+            sel = np.zeros((P, NG), np.uint8)
+            for i in range(P):
+                for J in range(NG):
+                    sel[i, J] = all(M[i, j] == dita.REUSE for M in later
+                                    for j in range(J * g, min(P, J * g + g)))
+            merge_sel.append((g, sel))
+        schedule_desc += "; after the anchor, cached states merged in groups of " + \
+            " then ".join(str(g) for g in merge_sizes)
     dense_flops = 4.0 * B * H * N * N * D
     stream = torch.cuda.current_stream()
     step_masks = []
@@ -174,9 +195,13 @@ def main():
         if s == 0:
             cache.reset()
         cache.set_policy(policies[s])
-        step_masks.append(cache.plan()["mask"])      # host copy of the plan, no device wait
+        pl = cache.plan()                             # host copy of the plan, no device wait
+        step_masks.append((pl["mask"], pl["reuse_ptr"]))
         q, kk, v = dev[s]
         cache.step(q, kk, v, out=out, lse=lse, stream=stream)
+        if s == 0:
+            for g, sel in merge_sel:
+                cache.merge_groups(g, select=sel, stream=stream)
 
     for k in range(args.warmup):
         run_step(k)
@@ -210,7 +235,7 @@ def main():
     ms_per_step = wall * 1e3 / K
     value = dense_flops * K / wall / 1e12
 
-    work = [mask_work(m, n_part, B * H, D, 2 if bf else 4) for m in step_masks[-K:]]
+    work = [mask_work(m, rp, n_part, B * H, D, 2 if bf else 4) for m, rp in step_masks[-K:]]
     fresh_flops = sum(w[0] for w in work)
     cache_bytes = sum(w[1] + w[2] for w in work)
     kern_ms = st["step_kernel_ms"]

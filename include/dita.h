@@ -239,7 +239,8 @@ dita_status dita_cache_read_slot(dita_cache* cache, int32_t b, int32_t h, int32_
  * group's first active member.  From then on the group is one state: a REUSE of its members
  * reads it once (dita_get_block_plan lists the group's first member only), and a step whose
  * policy makes any member FRESH recomputes every member, which dissolves the group.
- * Stream-ordered on hip_stream.  Errors: INVALID_ARGUMENT, DEVICE. */
+ * Stream-ordered on hip_stream.  Must be called between steps (no policy pending).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (B*H or max partition rows / 32 above 65535), DEVICE. */
 dita_status dita_cache_merge_groups(dita_cache* cache, int32_t group, const uint8_t* select,
                                     int32_t* merged, void* hip_stream);
 

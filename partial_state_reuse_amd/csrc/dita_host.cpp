@@ -1036,6 +1036,8 @@ dita_status dita_cache_merge_groups(dita_cache* c, int32_t group, const uint8_t*
   if (group < 2) return fail(DITA_ERR_INVALID_ARGUMENT, "group must be >= 2");
   if (c->has_pending)
     return fail(DITA_ERR_INVALID_ARGUMENT, "merge between steps, before the next policy is set");
+  if ((int64_t)c->g.B * c->g.H > 65535 || c->g.slot_rows / 32 > 65535)
+    return fail(DITA_ERR_UNSUPPORTED, "group composition supports B*H and rows/32 up to 65535");
   const int P = c->g.P;
   const int NG = (P + group - 1) / group;
   std::vector<int32_t> jobs, srcs;

@@ -88,7 +88,7 @@ inline int planner_chunks(int P) { return P >= 2048 ? 1 : (2048 / P > 64 ? 64 : 
 hipError_t launch_planner_delta(const StepArgs& a, float* delta, hipStream_t s);
 hipError_t launch_planner_weights(const StepArgs& a, float* w, float* part, hipStream_t s);
 // Group composition: job k = jobs[4k..4k+3] = {n_i, dst slot, first source, sources}; the
-// sources are slot numbers in srcs.  Grid (njobs, B*H).
+// sources are slot numbers in srcs.  Grid (njobs, slot_rows / 32 sub-tiles, B*H).
 hipError_t launch_merge_slots(const StepArgs& a, const int32_t* jobs, const int32_t* srcs,
                               int njobs, bool bf16, hipStream_t s);
 hipError_t launch_read_slot(const StepArgs& a, int bh, int slot, int i, float* o_out,

@@ -837,79 +837,77 @@ __global__ __launch_bounds__(256) void planner_weights_sum(StepArgs a, const flo
 
 // ------------------------------------------------------------------------------------------
 // group composition: merge cached states of one row partition into one slot
-// workgroup (k, bh): job k = {n_i, dst slot, first source, number of sources}; sources are
-// slots (the destination among them).  Per row: L = log sum_s exp(lse_s), O = sum_s
-// exp(lse_s - L) O_s in f32, stored rounded to the cache precision.  Rows are taken 32 at a
-// time: every lse is read before the destination's is written, and each O element is read
-// and written by the same thread.
+// workgroup (k, u, bh): 32-row sub-tile u of job k = {n_i, dst slot, first source, number
+// of sources}; sources are slots (the destination among them).  Per row: L = log sum_s
+// exp(lse_s), O = sum_s exp(lse_s - L) O_s in f32, stored rounded to the cache precision.
+// Every lse is read before the destination's is written, and each O element is read and
+// written by the same thread.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_slots(StepArgs a, const int32_t* jobs,
                                                    const int32_t* srcs, int bf16) {
   __shared__ float Ls[32];
-  const int k = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int k = blockIdx.x, u = blockIdx.y, bh = blockIdx.z, tid = threadIdx.x;
   const int n_i = jobs[4 * k], dst = jobs[4 * k + 1], s0 = jobs[4 * k + 2], ns = jobs[4 * k + 3];
+  if (u * 32 >= n_i) return;                    // workgroup-uniform
   const int DP = a.DP;
   const size_t slot_elems = (size_t)a.slot_rows * DP;
   auto lse_of = [&](int slot, int row) {
     return a.cache_lse[((size_t)bh * a.num_slots + slot) * a.slot_rows + row];
   };
-  for (int u = 0; u * 32 < n_i; ++u) {
-    if (tid < 32) {
-      const int row = u * 32 + tid;
-      float L = kNegInf;
-      if (row < n_i) {
-        float mx = kNegInf;
-        for (int q = 0; q < ns; ++q) mx = fmaxf(mx, lse_of(srcs[s0 + q], row));
-        float sum = 0.f;
-        for (int q = 0; q < ns; ++q) sum += expf(lse_of(srcs[s0 + q], row) - mx);
-        L = mx + logf(sum);
-      }
-      Ls[tid] = L;
+  if (tid < 32) {
+    const int row = u * 32 + tid;
+    float L = kNegInf;
+    if (row < n_i) {
+      float mx = kNegInf;
+      for (int q = 0; q < ns; ++q) mx = fmaxf(mx, lse_of(srcs[s0 + q], row));
+      float sum = 0.f;
+      for (int q = 0; q < ns; ++q) sum += expf(lse_of(srcs[s0 + q], row) - mx);
+      L = mx + logf(sum);
     }
-    __syncthreads();
-    if (bf16) {
-      uint16_t* cache = (uint16_t*)a.cache_o;
-      // the sub-tile is [DP/32 d tiles][64 lanes][16 values]; 16-byte chunk c: d tile c/128,
-      // lane (c/2)%64, half c%2; lane l holds query row l%32
-      for (int c = tid; c < DP * 4; c += 256) {
-        const int dt = c >> 7, lane = (c >> 1) & 63, half = c & 1;
-        const int r = lane & 31, row = u * 32 + r;
-        if (row >= n_i) continue;
-        const size_t off = (size_t)u * 32 * DP + dt * 1024 + lane * 16 + half * 8;
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < ns; ++q) {
-          const int sl = srcs[s0 + q];
-          const float w = expf(lse_of(sl, row) - Ls[r]);
-          const bf16x8 v = as_bf16x8(ld16(cache + ((size_t)bh * a.num_slots + sl) * slot_elems + off));
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)v[e], acc[e]);
-        }
-        u32x4 o;
-        uint16_t* op = (uint16_t*)&o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) op[e] = __builtin_bit_cast(uint16_t, (__bf16)acc[e]);
-        st16(cache + ((size_t)bh * a.num_slots + dst) * slot_elems + off, o);
-      }
-    } else {
-      float* cache = (float*)a.cache_o;
-      for (int e = tid; e < DP * 32; e += 256) {
-        const int d = e >> 5, r = e & 31, row = u * 32 + r;
-        if (row >= n_i) continue;
-        float acc = 0.f;
-        for (int q = 0; q < ns; ++q) {
-          const int sl = srcs[s0 + q];
-          acc = __builtin_fmaf(expf(lse_of(sl, row) - Ls[r]),
-                               cache[((size_t)bh * a.num_slots + sl) * slot_elems + (size_t)d * a.slot_rows + row],
-                               acc);
-        }
-        cache[((size_t)bh * a.num_slots + dst) * slot_elems + (size_t)d * a.slot_rows + row] = acc;
-      }
-    }
-    __syncthreads();
-    if (tid < 32 && u * 32 + tid < n_i)
-      a.cache_lse[((size_t)bh * a.num_slots + dst) * a.slot_rows + u * 32 + tid] = Ls[tid];
-    __syncthreads();
+    Ls[tid] = L;
   }
+  __syncthreads();
+  if (bf16) {
+    uint16_t* cache = (uint16_t*)a.cache_o;
+    // the sub-tile is [DP/32 d tiles][64 lanes][16 values]; 16-byte chunk c: d tile c/128,
+    // lane (c/2)%64, half c%2; lane l holds query row l%32
+    for (int c = tid; c < DP * 4; c += 256) {
+      const int dt = c >> 7, lane = (c >> 1) & 63, half = c & 1;
+      const int r = lane & 31, row = u * 32 + r;
+      if (row >= n_i) continue;
+      const size_t off = (size_t)u * 32 * DP + dt * 1024 + lane * 16 + half * 8;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < ns; ++q) {
+        const int sl = srcs[s0 + q];
+        const float w = expf(lse_of(sl, row) - Ls[r]);
+        const bf16x8 v = as_bf16x8(ld16(cache + ((size_t)bh * a.num_slots + sl) * slot_elems + off));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)v[e], acc[e]);
+      }
+      u32x4 o;
+      uint16_t* op = (uint16_t*)&o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) op[e] = __builtin_bit_cast(uint16_t, (__bf16)acc[e]);
+      st16(cache + ((size_t)bh * a.num_slots + dst) * slot_elems + off, o);
+    }
+  } else {
+    float* cache = (float*)a.cache_o;
+    for (int e = tid; e < DP * 32; e += 256) {
+      const int d = e >> 5, r = e & 31, row = u * 32 + r;
+      if (row >= n_i) continue;
+      float acc = 0.f;
+      for (int q = 0; q < ns; ++q) {
+        const int sl = srcs[s0 + q];
+        acc = __builtin_fmaf(expf(lse_of(sl, row) - Ls[r]),
+                             cache[((size_t)bh * a.num_slots + sl) * slot_elems + (size_t)d * a.slot_rows + row],
+                             acc);
+      }
+      cache[((size_t)bh * a.num_slots + dst) * slot_elems + (size_t)d * a.slot_rows + row] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < 32 && u * 32 + tid < n_i)
+    a.cache_lse[((size_t)bh * a.num_slots + dst) * a.slot_rows + u * 32 + tid] = Ls[tid];
 }
 
 }  // namespace
@@ -968,8 +966,8 @@ hipError_t launch_planner_weights(const StepArgs& a, float* w, float* part, hipS
 
 hipError_t launch_merge_slots(const StepArgs& a, const int32_t* jobs, const int32_t* srcs,
                               int njobs, bool bf16, hipStream_t s) {
-  hipLaunchKernelGGL(merge_slots, dim3(njobs, a.B * a.H), dim3(256), 0, s, a, jobs, srcs,
-                     bf16 ? 1 : 0);
+  hipLaunchKernelGGL(merge_slots, dim3(njobs, a.slot_rows / 32, a.B * a.H), dim3(256), 0, s, a,
+                     jobs, srcs, bf16 ? 1 : 0);
   return hipGetLastError();
 }
 
