@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--policy", choices=["schedule", "planner"], default="schedule",
                     help="schedule: the workload's fixed block schedule (the bench line); "
                          "planner: the selection planner at the same reuse budget")
+    ap.add_argument("--cache", choices=["bf16", "fp8"], default="bf16",
+                    help="cached O precision: bf16 (the bench line) or fp8 e4m3 (compressed)")
     ap.add_argument("--merge", type=str, default="",
                     help="comma-separated group sizes (e.g. 2,4): after each run's anchor step, "
                          "merge the cached states of every aligned key group that the schedule "
@@ -124,6 +126,9 @@ def main():
         sys.exit(2)
 
     cfg = CONFIGS[args.workload]
+    if args.cache == "fp8":
+        import dataclasses
+        cfg = dataclasses.replace(cfg, cache_dtype="fp8")
     S = cfg.steps
     B, H, N, D = cfg.batch, cfg.heads, cfg.tokens, cfg.head_dim
     # the worker pool is forked before this process touches the GPU
@@ -235,7 +240,8 @@ def main():
     ms_per_step = wall * 1e3 / K
     value = dense_flops * K / wall / 1e12
 
-    work = [mask_work(m, rp, n_part, B * H, D, 2 if bf else 4) for m, rp in step_masks[-K:]]
+    cache_elem = {"bf16": 2, "fp8": 1}.get(cfg.cache_dtype, 4)
+    work = [mask_work(m, rp, n_part, B * H, D, cache_elem) for m, rp in step_masks[-K:]]
     fresh_flops = sum(w[0] for w in work)
     cache_bytes = sum(w[1] + w[2] for w in work)
     kern_ms = st["step_kernel_ms"]
@@ -267,7 +273,7 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "heads": H, "tokens": N, "head_dim": D,
                    "partitions": cfg.num_partitions, "denoise_steps": S,
                    "schedule": schedule_desc,
-                   "cache": "bf16 O + f32 lse", "out": "f32"},
+                   "cache": f"{cfg.cache_dtype} O + f32 lse", "out": "f32"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

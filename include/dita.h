@@ -53,7 +53,11 @@ typedef enum dita_status {
   DITA_ERR_DEVICE = 8            /* a HIP call failed (message in dita_last_error)             */
 } dita_status;
 
-typedef enum dita_dtype { DITA_F32 = 0, DITA_BF16 = 1 } dita_dtype;
+/* DITA_FP8_E4M3: cache O only (with bf16 Q/K/V): OCP e4m3fn (1 sign, 4 exponent bits of bias
+ * 7, 3 mantissa bits; largest 448, no infinity), rounded to nearest even and saturated at
+ * +-448 -- a compressed state cache (DiTango, "Significato e Claim": cache compression named
+ * as a way to ease the state cache's memory cost). */
+typedef enum dita_dtype { DITA_F32 = 0, DITA_BF16 = 1, DITA_FP8_E4M3 = 2 } dita_dtype;
 
 enum { DITA_SKIP = 0, DITA_FRESH = 1, DITA_REUSE = 2 };
 
@@ -79,7 +83,8 @@ typedef struct dita_geometry {
                                                N mod P partitions get one more token).
                                                Copied; not kept.                           */
   dita_dtype qkv_dtype;                     /* element type of Q, K, V                      */
-  dita_dtype cache_o_dtype;                 /* must equal qkv_dtype; cache lse is f32       */
+  dita_dtype cache_o_dtype;                 /* qkv_dtype, or FP8_E4M3 with bf16 Q/K/V;
+                                               cache lse is f32                             */
   float softmax_scale;                      /* tau; <= 0 selects 1/sqrt(D)                  */
 } dita_geometry;
 

@@ -29,13 +29,13 @@ anchor.
 """
 from .policy import (partition_offsets, centroids2, partition_frames, active_mask,
                      policy_mask, work_lists, PolicyError, SKIP, FRESH, REUSE)
-from .attention import (block_state, merge_states, round_bf16, round_f32, run_head,
-                        OracleStep)
+from .attention import (block_state, merge_states, round_bf16, round_f32, round_fp8_e4m3,
+                        run_head, OracleStep)
 from .planner import (importance, growth, predicted_errors, planner_mask, run_planner,
                       PlannerStep, PLANNER)
 
 __all__ = ["partition_offsets", "centroids2", "partition_frames", "active_mask",
            "policy_mask", "work_lists", "PolicyError", "SKIP", "FRESH", "REUSE",
-           "block_state", "merge_states", "round_bf16", "round_f32", "run_head",
+           "block_state", "merge_states", "round_bf16", "round_f32", "round_fp8_e4m3", "run_head",
            "OracleStep", "importance", "growth", "predicted_errors", "planner_mask",
            "run_planner", "PlannerStep", "PLANNER"]

@@ -80,6 +80,24 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return rounded.view(np.float64)
 
 
+def round_fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even to OCP fp8 e4m3fn, saturating at +-448, widened back to float64.
+
+    e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; normal values
+    (1 + m/8) 2^(e-7) for e = 1..15 (largest 448 = 1.75 * 2^8), subnormals m/8 * 2^-6 (spacing
+    2^-9), no infinity.  In a binade [2^k, 2^(k+1)), k >= -6, the spacing is 2^(k-3); below
+    2^-6 it is 2^-9.  Values are rounded to a multiple of the spacing with ties to even."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("round_fp8_e4m3: non-finite input")
+    ax = np.abs(x)
+    k = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    spacing = np.exp2(np.maximum(k, -6.0) - 3.0)
+    r = np.round(ax / spacing) * spacing           # numpy rounds halves to even
+    r = np.minimum(r, 448.0)
+    return np.copysign(r, x)
+
+
 @dataclass
 class OracleStep:
     step: int
@@ -93,6 +111,7 @@ class OracleStep:
     out: np.ndarray                   # float64 [len(rows), D]
     lse: np.ndarray                   # float64 [len(rows)]
     block_lse: dict = field(default_factory=dict)   # (i, j) -> lse rows used this step
+    block_o: dict = field(default_factory=dict)     # (i, j) -> O rows used (keep_block_lse)
 
 
 def merge_groups(cache, head, P, act, group, select, rho_o, rho_l, step):
@@ -152,7 +171,7 @@ def run_head(cfg, b: int, h: int, steps: int | None = None, rows=None,
     if cache_mode == "fp64":
         rho_o, rho_l = (lambda a: np.array(a, dtype=np.float64)), (lambda a: np.array(a))
     elif cache_mode == "emulate":
-        rho_o = round_bf16 if cfg.cache_dtype == "bf16" else round_f32
+        rho_o = {"bf16": round_bf16, "fp8": round_fp8_e4m3}.get(cfg.cache_dtype, round_f32)
         rho_l = round_f32
     else:
         raise ValueError(cache_mode)
@@ -197,6 +216,7 @@ def run_head(cfg, b: int, h: int, steps: int | None = None, rows=None,
         out = np.zeros((len(rows), D))
         lse = np.full(len(rows), -np.inf)
         blk = {}
+        blk_o = {}
         pos = 0
         for i in range(P):
             r = part_rows[i]
@@ -216,12 +236,13 @@ def run_head(cfg, b: int, h: int, steps: int | None = None, rows=None,
                 states.append((O_ij, l_ij))
                 if keep_block_lse:
                     blk[(i, j)] = l_ij
+                    blk_o[(i, j)] = O_ij
             if len(r):
                 o_i, L_i = merge_states(states)
                 out[pos:pos + len(r)] = o_i
                 lse[pos:pos + len(r)] = L_i
             pos += len(r)
-        results.append(OracleStep(s, M, fp, fc, rp, rc, counts, rows, out, lse, blk))
+        results.append(OracleStep(s, M, fp, fc, rp, rc, counts, rows, out, lse, blk, blk_o))
         for (g, sel) in (merges or {}).get(s, []):
             merge_groups(cache, head, P, act, g, sel, rho_o, rho_l, s)
     return results

@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .attention import block_state, merge_states, round_bf16, round_f32
+from .attention import block_state, merge_states, round_bf16, round_f32, round_fp8_e4m3
 from .policy import FRESH, REUSE, SKIP, active_mask, partition_offsets, PolicyError
 
 PLANNER = 4
@@ -164,7 +164,7 @@ def run_planner(cfg, heads, policy, steps=None, cache_mode="emulate", masks=None
     if cache_mode == "fp64":
         rho_o, rho_l = (lambda a: np.array(a, dtype=np.float64)), (lambda a: np.array(a))
     else:
-        rho_o = round_bf16 if cfg.cache_dtype == "bf16" else round_f32
+        rho_o = {"bf16": round_bf16, "fp8": round_fp8_e4m3}.get(cfg.cache_dtype, round_f32)
         rho_l = round_f32
     if inputs is None:
         from workloads.gen import HeadStream

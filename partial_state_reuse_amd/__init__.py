@@ -26,7 +26,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK = 0
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "SHAPE", 3: "UNSUPPORTED", 4: "POLICY",
                 5: "CACHE_MISS", 6: "BUFFER_TOO_SMALL", 7: "NO_POLICY", 8: "DEVICE"}
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
+_DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 SKIP, FRESH, REUSE = 0, 1, 2
 POLICY_EXPLICIT, POLICY_FRAME_THRESHOLD, POLICY_FRESH_BUDGET, POLICY_CENTROID_THRESHOLD = 0, 1, 2, 3
 POLICY_PLANNER = 4
@@ -125,13 +126,17 @@ def _u8(arr):
 
 
 def make_geometry(batch, heads, tokens, head_dim, frames, grid_h, grid_w, num_partitions,
-                  dtype="bf16", offsets=None, softmax_scale=0.0):
-    """A Geometry; `offsets` (P+1 ints) or None for the array_split rule."""
+                  dtype="bf16", offsets=None, softmax_scale=0.0, cache_dtype=None):
+    """A Geometry; `offsets` (P+1 ints) or None for the array_split rule; `cache_dtype`
+    (cached O) defaults to `dtype` ("fp8" = e4m3, with bf16 Q/K/V)."""
     g = Geometry()
     g.batch, g.heads, g.tokens, g.head_dim = batch, heads, tokens, head_dim
     g.frames, g.grid_h, g.grid_w, g.num_partitions = frames, grid_h, grid_w, num_partitions
-    dt = {"bf16": BF16, "f32": F32}[dtype] if isinstance(dtype, str) else int(dtype)
-    g.qkv_dtype = g.cache_o_dtype = dt
+    dt = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    cd = dt if cache_dtype is None else (_DTYPES[cache_dtype] if isinstance(cache_dtype, str)
+                                         else int(cache_dtype))
+    g.qkv_dtype = dt
+    g.cache_o_dtype = cd
     g.softmax_scale = softmax_scale
     if offsets is not None:
         arr = (ctypes.c_int32 * len(offsets))(*[int(x) for x in offsets])
@@ -369,4 +374,4 @@ def geometry_from(cfg, offsets=None) -> Geometry:
     """Geometry from any object with the fields of workloads.Config."""
     return make_geometry(cfg.batch, cfg.heads, cfg.tokens, cfg.head_dim, cfg.frames,
                          cfg.grid_h, cfg.grid_w, cfg.num_partitions, cfg.qkv_dtype,
-                         offsets=offsets)
+                         offsets=offsets, cache_dtype=getattr(cfg, "cache_dtype", None))

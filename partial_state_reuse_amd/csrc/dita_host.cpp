@@ -60,6 +60,8 @@ struct Geo {
   std::vector<int32_t> tails;        // {i, first row} per tail sub-tile, padded to 4 per wg
   int slot_rows = 0;
   bool bf16() const { return qkv == DITA_BF16; }
+  // bytes per cached O element
+  size_t cache_esz() const { return cache_o == DITA_FP8_E4M3 ? 1 : (cache_o == DITA_BF16 ? 2 : 4); }
 };
 
 dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
@@ -81,8 +83,10 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
   r.F = r.gh * r.gw;
   if (g->qkv_dtype != DITA_F32 && g->qkv_dtype != DITA_BF16)
     return fail(DITA_ERR_INVALID_ARGUMENT, "unknown qkv_dtype");
-  if (g->cache_o_dtype != g->qkv_dtype)
-    return fail(DITA_ERR_UNSUPPORTED, "cache_o_dtype must equal qkv_dtype");
+  if (g->cache_o_dtype != g->qkv_dtype &&
+      !(g->cache_o_dtype == DITA_FP8_E4M3 && g->qkv_dtype == DITA_BF16))
+    return fail(DITA_ERR_UNSUPPORTED, "cache_o_dtype must equal qkv_dtype, or be FP8_E4M3 with "
+                "bf16 Q/K/V");
   r.qkv = g->qkv_dtype;
   r.cache_o = g->cache_o_dtype;
   if (r.bf16()) {
@@ -372,7 +376,7 @@ Layout compute_layout(const Geo& g, int num_slots) {
   L.lse = at;
   at = align_up(at + bh * num_slots * (size_t)g.slot_rows * 4, 256);
   L.o = at;
-  const size_t esz = g.cache_o == DITA_BF16 ? 2 : 4;
+  const size_t esz = g.cache_esz();
   at = align_up(at + bh * num_slots * (size_t)g.slot_rows * g.DP * esz, 256);
   // planner measurement: per (b, h, i, 32-row sub-tile) squared changes, then the reduced
   // importance (P*P f32) and growth (P f32)
@@ -475,7 +479,7 @@ namespace {
 void plan_work(const dita_cache* c, const Plan& p, double* flops, double* rd, double* wr) {
   const Geo& g = c->g;
   const double bh = (double)g.B * g.H;
-  const double sc = g.cache_o == DITA_BF16 ? 2.0 : 4.0;
+  const double sc = (double)g.cache_esz();
   double f = 0, r = 0, w = 0;
   for (int i = 0; i < g.P; ++i) {
     const double ni = g.offs[i + 1] - g.offs[i];
@@ -552,6 +556,7 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->scale_log2 = g.tau * 1.4426950408889634f;
   a->delta_part = nullptr;
   a->delta_stride = g.slot_rows / 32;
+  a->cache_fp8 = g.cache_o == DITA_FP8_E4M3 ? 1 : 0;
 }
 
 dita_status hip_check(hipError_t e, const char* what) {
@@ -1014,7 +1019,7 @@ dita_status dita_cache_read_slot(dita_cache* c, int32_t b, int32_t h, int32_t i,
   const size_t hblk = (size_t)i * g.P + c->head[blk];   // a merged group's state
   return hip_check(dita::launch_read_slot(a, b * g.H + h, c->slot_of[hblk],
                                           g.offs[i + 1] - g.offs[i], o_out, lse_out,
-                                          g.bf16(), (hipStream_t)hip_stream),
+                                          (int)g.cache_esz(), (hipStream_t)hip_stream),
                    "read_slot launch");
 }
 
@@ -1105,7 +1110,8 @@ dita_status dita_cache_merge_groups(dita_cache* c, int32_t group, const uint8_t*
   if (st) return st;
   dita::StepArgs a{};
   fill_args(c, 0, &a);
-  st = hip_check(dita::launch_merge_slots(a, dev, dev + jobs.size(), njobs, c->g.bf16(), s),
+  st = hip_check(dita::launch_merge_slots(a, dev, dev + jobs.size(), njobs,
+                                          (int)c->g.cache_esz(), s),
                  "merge_slots launch");
   if (st) return st;
   st = hip_check(hipEventRecord(c->merge_event, s), "hipEventRecord");

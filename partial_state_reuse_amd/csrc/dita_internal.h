@@ -53,7 +53,8 @@ struct StepArgs {
   float* out;
   float* lse_out;            // may be null
   void* vt;                  // fp16 transposed-V scratch [B*H][DP][kt_pad]
-  void* cache_o;             // bf16: [B*H][slots][slot_rows/32][DP/32][64][16] fragment order
+  void* cache_o;             // bf16 / fp8: [B*H][slots][slot_rows/32][DP/32][64][16] elements
+                             //   in fragment order
                              // f32:  [B*H][slots][DP][slot_rows]
   float* cache_lse;          // [B*H][slots][slot_rows], natural log
   unsigned long long* counters;  // [0] fresh blocks, [1] reused blocks, [2] V elements
@@ -71,6 +72,7 @@ struct StepArgs {
   // (new cached O - old cached O)^2 at delta_part[(bh * P + i) * delta_stride + row / 32].
   float* delta_part;
   int32_t delta_stride;      // slot_rows / 32
+  int32_t cache_fp8;         // bf16 path: cached O as fp8 e4m3 (1) or bf16 (0)
 };
 
 hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s);
@@ -90,8 +92,8 @@ hipError_t launch_planner_weights(const StepArgs& a, float* w, float* part, hipS
 // Group composition: job k = jobs[4k..4k+3] = {n_i, dst slot, first source, sources}; the
 // sources are slot numbers in srcs.  Grid (njobs, slot_rows / 32 sub-tiles, B*H).
 hipError_t launch_merge_slots(const StepArgs& a, const int32_t* jobs, const int32_t* srcs,
-                              int njobs, bool bf16, hipStream_t s);
+                              int njobs, int cache_esz, hipStream_t s);
 hipError_t launch_read_slot(const StepArgs& a, int bh, int slot, int i, float* o_out,
-                            float* lse_out, bool bf16, hipStream_t s);
+                            float* lse_out, int cache_esz, hipStream_t s);
 
 }  // namespace dita

@@ -177,15 +177,44 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// fp8 e4m3 cache elements: 16 f32 values of a lane's fragment <-> 16 bytes, value r in byte
+// r, with the hardware conversion (round to nearest even, saturating at +-448).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 fp8_pack16(const f32x16& v) {
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k], v[4 * k + 1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k + 2], v[4 * k + 3], w, true);
+    o[k] = (uint32_t)w;
+  }
+  return o;
+}
+__device__ __forceinline__ void fp8_unpack16(u32x4 w, float* v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+    v[4 * k] = lo[0];
+    v[4 * k + 1] = lo[1];
+    v[4 * k + 2] = hi[0];
+    v[4 * k + 3] = hi[1];
+  }
+}
+// element type of the cached O: bf16 bits, or fp8 bytes
+template <bool FP8> struct CacheElem { typedef uint16_t type; };
+template <> struct CacheElem<true> { typedef uint8_t type; };
+
 // Block end, for the wave's 32-row sub-tile: normalise the block state, store it to its
-// slot (O^T fragment as bf16 in fragment order, lse as f32 natural log) and fold it into
+// slot (O^T fragment as bf16 or fp8 in fragment order, lse as f32 natural log) and fold it into
 // the row's running merge (base-2 units).  For a diagonal block with the planner measurement
 // on, the squared change of the cached O (new - old, over rows < n_i and dims < D) is summed
 // first and stored for the sub-tile.
-template <int NDT, bool MEASURE>
+template <int NDT, bool MEASURE, bool FP8>
 __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT], float m_b,
                                           float l_b, int paddr, size_t slot_base, int row0,
-                                          int myrow, uint16_t* dst, f32x16 (&acc)[NDT],
+                                          int myrow, typename CacheElem<FP8>::type* dst,
+                                          f32x16 (&acc)[NDT],
                                           float& m_row, float& l_row, bool diag, int n_i,
                                           int i, int bh) {
   const int lane = threadIdx.x & 63, h32 = lane >> 5;
@@ -197,6 +226,22 @@ __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT]
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     bacc[dt] *= inv;
+    if constexpr (FP8) {
+      const u32x4 w = fp8_pack16(bacc[dt]);
+      if (measure) {
+        float nv[16], ov[16];
+        fp8_unpack16(w, nv);
+        fp8_unpack16(ld16(dst + dt * 1024 + lane * 16), ov);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = dt * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          const float df = nv[r] - ov[r];
+          if (myrow < n_i && d < a.D) sq = __builtin_fmaf(df, df, sq);
+        }
+      }
+      st16(dst + dt * 1024 + lane * 16, w);
+      continue;
+    }
     u32x4 w0, w1;
     uint16_t* e0p = (uint16_t*)&w0;
     uint16_t* e1p = (uint16_t*)&w1;
@@ -234,7 +279,7 @@ __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT]
 
 // Reused blocks folded into the row's merge, then the epilogue (out = acc / l, lse) and the
 // per-partition block counts, for the wave's 32-row sub-tile.
-template <int DP>
+template <int DP, bool FP8>
 __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int i, int o_i,
                                                  int n_i, int row0, int e0, int nf, int nr,
                                                  f32x16 (&acc)[DP / 32], float m_row,
@@ -244,12 +289,30 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
   const int myrow = row0 + l32;
   const cint* ent = as_const(a.plan) + a.off_ent;
   const size_t slot_elems = (size_t)a.slot_rows * DP;
-  const uint16_t* cache_o = (const uint16_t*)a.cache_o;
+  typedef typename CacheElem<FP8>::type CT;
+  const CT* cache_o = (const CT*)a.cache_o;
   for (int e = nf; e < nf + nr; ++e) {
     const int slot = ent[2 * (e0 + e) + 1];
     const size_t slot_base = (size_t)bh * a.num_slots + slot;
     const float lse2 = a.cache_lse[slot_base * a.slot_rows + myrow] * kLog2e;
-    const uint16_t* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
+    const CT* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
+    if constexpr (FP8) {
+      u32x4 raw8[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) raw8[dt] = ld16(src + dt * 1024 + lane * 16);
+      const float mn = fmaxf(m_row, lse2);
+      const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        float v[16];
+        fp8_unpack16(raw8[dt], v);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = acc[dt][r] * fa + v[r] * fb;
+      }
+      l_row = l_row * fa + fb;
+      m_row = mn;
+      continue;
+    }
     u32x4 raw[NDT][2];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -299,7 +362,7 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
 // Tail workgroup: 4 independent waves, each with its own 32-row sub-tile (possibly of
 // different partitions); each reads its K / V^T fragments straight from global memory (L2),
 // with no LDS and no barrier.
-template <int DP, bool MEASURE>
+template <int DP, bool MEASURE, bool FP8>
 __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
   constexpr int NKC = DP / 16, NDT = DP / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -337,7 +400,7 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x16){};
   float m_row = kNegInf, l_row = 0.f;
   const size_t slot_elems = (size_t)a.slot_rows * DP;
-  uint16_t* cache_o = (uint16_t*)a.cache_o;
+  typename CacheElem<FP8>::type* cache_o = (typename CacheElem<FP8>::type*)a.cache_o;
   const uint16_t* Kg = (const uint16_t*)a.k + bhN * a.D;
   const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
 
@@ -408,16 +471,17 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
         for (int c = 0; c < 2; ++c)
           bacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[dt][c], pf[c], bacc[dt], 0, 0, 0);
     }
-    block_end<NDT, MEASURE>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
+    block_end<NDT, MEASURE, FP8>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
                    cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
                    acc, m_row, l_row, j == i, n_i, i, bh);
   }
-  reuse_and_finish<DP>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
+  reuse_and_finish<DP, FP8>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
 }
 
 // MEASURE: the planner's measurement of the diagonal states' change is compiled in (a
 // separate instantiation, so that steps without it keep the leaner register allocation).
-template <int DP, bool MEASURE>
+// FP8: the cached O is fp8 e4m3 instead of bf16.
+template <int DP, bool MEASURE, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 3 : 1))) void step_bf16(StepArgs a) {
   constexpr int NKC = DP / 16;        // 16-wide d chunks of Q K^T
   constexpr int NDT = DP / 32;        // 32-row d tiles of O^T
@@ -440,7 +504,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const cint* poffs = plan + a.off_poffs;
   const int packed = plan[a.off_tiles + tix];
   if (packed & kTailFlag) {                     // workgroup-uniform
-    tail_wave<DP, MEASURE>(a, bh, packed & 0xffff);
+    tail_wave<DP, MEASURE, FP8>(a, bh, packed & 0xffff);
     return;
   }
   const int i = packed >> 16, t = packed & 0xffff;
@@ -477,7 +541,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   float m_row = kNegInf, l_row = 0.f;
 
   const size_t slot_elems = (size_t)a.slot_rows * DP;
-  uint16_t* cache_o = (uint16_t*)a.cache_o;
+  typename CacheElem<FP8>::type* cache_o = (typename CacheElem<FP8>::type*)a.cache_o;
   const uint16_t* Kg = (const uint16_t*)a.k + bhN * a.D;
   const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
 
@@ -580,13 +644,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     }
     if (!live) continue;
 
-    block_end<NDT, MEASURE>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
+    block_end<NDT, MEASURE, FP8>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
                    cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
                    acc, m_row, l_row, j == i, n_i, i, bh);
   }
   if (!live) return;
 
-  reuse_and_finish<DP>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
+  reuse_and_finish<DP, FP8>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -723,7 +787,7 @@ __global__ __launch_bounds__(64) void step_f32(StepArgs a) {
 // read one cache slot into row-major f32 (n_i x D) and lse (n_i)
 // ------------------------------------------------------------------------------------------
 __global__ void read_slot(StepArgs a, int bh, int slot, int n_i, float* o_out, float* lse_out,
-                          int bf16) {
+                          int esz) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int D = a.D, DP = a.DP;
   const size_t base = (size_t)bh * a.num_slots + slot;
@@ -731,13 +795,20 @@ __global__ void read_slot(StepArgs a, int bh, int slot, int n_i, float* o_out, f
   if (idx >= n_i * D) return;
   const int row = idx / D, d = idx - row * D;
   float val;
-  if (bf16) {
-    const uint16_t* src = (const uint16_t*)a.cache_o + base * (size_t)a.slot_rows * DP;
+  if (esz != 4) {
+    // fragment order: sub-tile row/32, d tile d/32, lane (d%32/4 odd ? 32 : 0) + row%32,
+    // value 4*(d%32/8) + d%4
     const int u = row >> 5, l32 = row & 31, dt = d >> 5, dd = d & 31;
     const int h = (dd >> 2) & 1, reg = 4 * (dd >> 3) + (dd & 3);
     const int lane = h * 32 + l32;
-    const uint16_t bits = src[(size_t)u * 32 * DP + dt * 1024 + lane * 16 + reg];
-    val = (float)__builtin_bit_cast(__bf16, bits);
+    const size_t off = base * (size_t)a.slot_rows * DP + (size_t)u * 32 * DP + dt * 1024 + lane * 16;
+    if (esz == 2) {
+      val = (float)__builtin_bit_cast(__bf16, ((const uint16_t*)a.cache_o)[off + reg]);
+    } else {
+      float v[16];
+      fp8_unpack16(ld16((const uint8_t*)a.cache_o + off), v);
+      val = v[reg];
+    }
   } else {
     const float* src = (const float*)a.cache_o + base * (size_t)DP * a.slot_rows;
     val = src[(size_t)d * a.slot_rows + row];
@@ -844,7 +915,7 @@ __global__ __launch_bounds__(256) void planner_weights_sum(StepArgs a, const flo
 // written by the same thread.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_slots(StepArgs a, const int32_t* jobs,
-                                                   const int32_t* srcs, int bf16) {
+                                                   const int32_t* srcs, int esz) {
   __shared__ float Ls[32];
   const int k = blockIdx.x, u = blockIdx.y, bh = blockIdx.z, tid = threadIdx.x;
   const int n_i = jobs[4 * k], dst = jobs[4 * k + 1], s0 = jobs[4 * k + 2], ns = jobs[4 * k + 3];
@@ -867,7 +938,26 @@ __global__ __launch_bounds__(256) void merge_slots(StepArgs a, const int32_t* jo
     Ls[tid] = L;
   }
   __syncthreads();
-  if (bf16) {
+  if (esz == 1) {
+    uint8_t* cache = (uint8_t*)a.cache_o;
+    // fp8: 16-byte chunk c = one lane's 16 values of d tile c/64 (lane c%64, row lane%32)
+    for (int c = tid; c < DP * 2; c += 256) {
+      const int dt = c >> 6, lane = c & 63;
+      const int r = lane & 31, row = u * 32 + r;
+      if (row >= n_i) continue;
+      const size_t off = (size_t)u * 32 * DP + dt * 1024 + lane * 16;
+      f32x16 acc = (f32x16){};
+      for (int q = 0; q < ns; ++q) {
+        const int sl = srcs[s0 + q];
+        const float w = expf(lse_of(sl, row) - Ls[r]);
+        float v[16];
+        fp8_unpack16(ld16(cache + ((size_t)bh * a.num_slots + sl) * slot_elems + off), v);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
+      }
+      st16(cache + ((size_t)bh * a.num_slots + dst) * slot_elems + off, fp8_pack16(acc));
+    }
+  } else if (esz == 2) {
     uint16_t* cache = (uint16_t*)a.cache_o;
     // the sub-tile is [DP/32 d tiles][64 lanes][16 values]; 16-byte chunk c: d tile c/128,
     // lane (c/2)%64, half c%2; lane l holds query row l%32
@@ -925,22 +1015,21 @@ hipError_t launch_transpose_v(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s) {
   const int G = a.num_tiles * a.B * a.H;
-  const bool m = a.delta_part != nullptr;
+  const int m = a.delta_part != nullptr ? 1 : 0, f = a.cache_fp8 ? 2 : 0;
+#define DITA_LAUNCH_BF16(DPV)                                                                   \
+  switch (m | f) {                                                                              \
+    case 0: hipLaunchKernelGGL((step_bf16<DPV, false, false>), dim3(G), dim3(256), 0, s, a); break; \
+    case 1: hipLaunchKernelGGL((step_bf16<DPV, true, false>), dim3(G), dim3(256), 0, s, a); break;  \
+    case 2: hipLaunchKernelGGL((step_bf16<DPV, false, true>), dim3(G), dim3(256), 0, s, a); break;  \
+    default: hipLaunchKernelGGL((step_bf16<DPV, true, true>), dim3(G), dim3(256), 0, s, a); break;  \
+  }
   switch (a.DP) {
-    case 64:
-      if (m) hipLaunchKernelGGL((step_bf16<64, true>), dim3(G), dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((step_bf16<64, false>), dim3(G), dim3(256), 0, s, a);
-      break;
-    case 96:
-      if (m) hipLaunchKernelGGL((step_bf16<96, true>), dim3(G), dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((step_bf16<96, false>), dim3(G), dim3(256), 0, s, a);
-      break;
-    case 128:
-      if (m) hipLaunchKernelGGL((step_bf16<128, true>), dim3(G), dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((step_bf16<128, false>), dim3(G), dim3(256), 0, s, a);
-      break;
+    case 64: DITA_LAUNCH_BF16(64) break;
+    case 96: DITA_LAUNCH_BF16(96) break;
+    case 128: DITA_LAUNCH_BF16(128) break;
     default: return hipErrorInvalidValue;
   }
+#undef DITA_LAUNCH_BF16
   return hipGetLastError();
 }
 
@@ -965,17 +1054,17 @@ hipError_t launch_planner_weights(const StepArgs& a, float* w, float* part, hipS
 }
 
 hipError_t launch_merge_slots(const StepArgs& a, const int32_t* jobs, const int32_t* srcs,
-                              int njobs, bool bf16, hipStream_t s) {
+                              int njobs, int cache_esz, hipStream_t s) {
   hipLaunchKernelGGL(merge_slots, dim3(njobs, a.slot_rows / 32, a.B * a.H), dim3(256), 0, s, a,
-                     jobs, srcs, bf16 ? 1 : 0);
+                     jobs, srcs, cache_esz);
   return hipGetLastError();
 }
 
 hipError_t launch_read_slot(const StepArgs& a, int bh, int slot, int n_i, float* o_out,
-                            float* lse_out, bool bf16, hipStream_t s) {
+                            float* lse_out, int cache_esz, hipStream_t s) {
   const int n = n_i * a.D;
   hipLaunchKernelGGL(read_slot, dim3((n + 255) / 256), dim3(256), 0, s, a, bh, slot, n_i,
-                     o_out, lse_out, bf16 ? 1 : 0);
+                     o_out, lse_out, cache_esz);
   return hipGetLastError();
 }
 

@@ -1,0 +1,117 @@
+"""GPU parity of the fp8 (e4m3) state cache, through the C ABI.
+
+The cache is lossy by design: the comparison is with the oracle that rounds its cached
+states to e4m3 the same way (nearest even, saturating).  The GPU and the oracle round values
+that differ by their arithmetic error, so a cached element can land one e4m3 spacing apart on
+the two sides; each reused state r enters the output with weight w_r = exp(lse_r - L), so the
+element-wise bar is the bf16 output bar plus sum over reused states of w_r * spacing(|O_r|).
+lse does not depend on the O rounding and keeps the bf16 bar.  The distance to the exact
+(fp64, unrounded) result is logged: it is the accuracy the compression costs."""
+import numpy as np
+import pytest
+
+import gpu_helpers as gh
+from gpu_helpers import BF16_MAX_ABS, BF16_MEAN_ABS, log
+from workloads import Policy, custom_config
+from workloads import configs as wcfg
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dita():
+    import partial_state_reuse_amd as d
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return d
+
+
+def spacing8(x):
+    ax = np.abs(np.asarray(x, np.float64))
+    k = np.floor(np.log2(np.where(ax > 0, ax, 2.0 ** -9)))
+    return np.exp2(np.maximum(k, -6.0) - 3.0)
+
+
+CASES = [
+    # name, frames, gh, gw, P, D, heads, steps, schedule, merges
+    ("fp8-d64-tails", 4, 10, 26, 8, 64, 2, 4, "budget", None),     # 130-row partitions
+    ("fp8-d128", 3, 8, 10, 6, 128, 2, 4, "frame", None),
+    ("fp8-d72", 2, 9, 11, 3, 72, 2, 3, "frame", None),
+    ("fp8-d64-merged", 8, 5, 7, 8, 64, 1, 4, "frame", {1: [(2, None)]}),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fp8_cache(dita, case):
+    import oracle
+    from oracle.policy import active_mask, partition_offsets
+    name, T, gh_, gw, P, D, H, S, kind, merges = case
+    if kind == "budget":
+        sched = wcfg.AnchorThen(Policy(kind=wcfg.FRESH_BUDGET, reuse_percent=60))
+    else:
+        sched = wcfg.AnchorThen(Policy(kind=wcfg.FRAME_THRESHOLD, max_fresh_frame_dist=1))
+    cfg = custom_config(name=name, idx=90, heads=H, head_dim=D, frames=T, grid_h=gh_, grid_w=gw,
+                        num_partitions=P, steps=S, qkv_dtype="bf16", cache_dtype="fp8",
+                        schedule=sched)
+    heads = [(0, h) for h in range(H)]
+    offs = partition_offsets(cfg.tokens, P)
+    act = active_mask(offs, cfg.frame_tokens, False)
+    log(f"case {name}: N={cfg.tokens} P={P} D={D} H={H} steps={S} cache fp8 merges={merges}")
+    dev, kept = gh.device_inputs(cfg, S, keep_heads=set(heads))
+    cache = dita.Cache(dita.geometry_from(cfg), active_mask=act.astype(np.uint8))
+    outs, lses, plans = [], [], []
+    for s in range(1, S + 1):
+        cache.set_policy(dita.policy_from(cfg.policy(s)))
+        plans.append(cache.plan())
+        q, k, v = dev[s - 1]
+        out, lse = cache.step(q, k, v)
+        outs.append(out.cpu().numpy())
+        lses.append(lse.cpu().numpy())
+        for (g, sel) in (merges or {}).get(s, []):
+            cache.merge_groups(g, select=sel)
+    # cached states written at the last step, read back
+    last = plans[-1]["mask"]
+    slots = {}
+    for (b, h) in heads[:1]:
+        for i in range(P):
+            for j in range(P):
+                if last[i, j] == 1:
+                    o_, l_ = cache.read_slot(b, h, i, j)
+                    slots[(i, j)] = (o_.cpu().numpy(), l_.cpu().numpy())
+    cache.free()
+
+    ok = True
+    for (b, h) in heads:
+        emu = oracle.run_head(cfg, b, h, cache_mode="emulate", merges=merges, active=act,
+                              inputs=kept[(b, h)], keep_block_lse=True)
+        exact = oracle.run_head(cfg, b, h, cache_mode="fp64", merges=merges, active=act,
+                                inputs=kept[(b, h)])
+        for s in range(S):
+            r = emu[s]
+            assert np.array_equal(plans[s]["mask"], r.mask), f"step {s + 1}: mask"
+            bound = np.full((cfg.tokens, D), BF16_MAX_ABS)
+            for i in range(P):
+                rows = slice(offs[i], offs[i + 1])
+                for j in range(P):
+                    if r.mask[i, j] == 2 and (i, j) in r.block_o:
+                        wgt = np.exp(r.block_lse[(i, j)] - r.lse[rows])
+                        bound[rows] += wgt[:, None] * spacing8(r.block_o[(i, j)])
+            err = np.abs(outs[s][b, h] - r.out)
+            slack = float((err - bound).max())
+            lerr = float(np.abs(lses[s][b, h] - r.lse).max())
+            xerr = np.abs(outs[s][b, h] - exact[s].out)
+            log(f"step {s + 1} head {h}: vs fp8 oracle max {err.max():.3e} mean {err.mean():.3e} "
+                f"(bar slack {slack:.2e}); lse {lerr:.2e}; vs exact max {xerr.max():.3e} "
+                f"mean {xerr.mean():.3e}")
+            ok &= slack <= 0 and lerr < 2e-3 and err.mean() <= BF16_MEAN_ABS
+        if (b, h) == heads[0]:
+            r = emu[-1]
+            for (i, j), (o_, l_) in slots.items():
+                want = oracle.round_fp8_e4m3(r.block_o[(i, j)])
+                d = np.abs(o_ - want)
+                assert np.all(d <= spacing8(want) + 1e-6), f"slot ({i},{j}) max {d.max():.3e}"
+                assert np.abs(l_ - r.block_lse[(i, j)]).max() < 2e-3
+            log(f"{len(slots)} cached fp8 states read back within one e4m3 spacing")
+    assert ok
