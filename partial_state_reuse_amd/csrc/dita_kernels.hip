@@ -380,6 +380,7 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
   const cint* ent = plan + a.off_ent;
   const size_t bhN = (size_t)bh * a.N;
   const float sc = a.scale_log2;
+  const float inv_sc = 1.0f / sc;
   const int paddr = partner_addr();
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
@@ -411,7 +412,7 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
     f32x16 bacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) bacc[dt] = (f32x16){};
-    float m_b = kNegInf, l_b = 0.f;
+    float m_b = kNegInf, l_b = 0.f, thr = kNegInf;
     for (int kbase = 0; kbase < n_j; kbase += 32) {
       // K fragments: row key_of_row(l32) of the unit (clamped into the block: keys past its
       // end are masked below), dims kc*16 + 8*h32 (clamped below D, where Q is zero)
@@ -442,14 +443,16 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
           if (key >= n_j) s[r] = kNegInf;
         }
       }
+      // this lane's max over its 16 keys against the rescale threshold (in score units);
+      // the query's exact max over both lanes is formed only when a rescale is due
       float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
       for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1 < 16 ? r + 1 : r]);
-      mx = max_halves(mx, paddr) * sc;
-      if (__any(mx > m_b + kRescaleSlack)) {
-        const float m_new = fmaxf(m_b, mx);
+      if (__any(mx > thr)) {
+        const float m_new = fmaxf(m_b, max_halves(mx, paddr) * sc);
         const float alpha = fast_exp2(m_b - m_new);
         m_b = m_new;
+        thr = (m_new + kRescaleSlack) * inv_sc;
         l_b *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= alpha;
@@ -517,6 +520,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const cint* ent = plan + a.off_ent;
   const size_t bhN = (size_t)bh * a.N;
   const float sc = a.scale_log2;
+  const float inv_sc = 1.0f / sc;
   const int paddr = partner_addr();
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
@@ -555,6 +559,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) bacc[dt] = (f32x16){};
     float m_b = kNegInf, l_b = 0.f;   // l_b: this lane's partial sum (16 of the 32 keys)
+    float thr = kNegInf;              // rescale threshold: (m_b + slack) / (tau log2 e)
 
     u32x4 pk[CHK], pv[CHV];
     auto fetch = [&](int kt) {
@@ -608,14 +613,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
             if (key >= n_j) s[r] = kNegInf;
           }
         }
+        // this lane's max over its 16 keys against the rescale threshold (in score units);
+        // the query's exact max over both lanes is formed only when a rescale is due
         float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
         for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1 < 16 ? r + 1 : r]);
-        mx = max_halves(mx, paddr) * sc;
-        if (__any(mx > m_b + kRescaleSlack)) {
-          const float m_new = fmaxf(m_b, mx);
+        if (__any(mx > thr)) {
+          const float m_new = fmaxf(m_b, max_halves(mx, paddr) * sc);
           const float alpha = fast_exp2(m_b - m_new);
           m_b = m_new;
+          thr = (m_new + kRescaleSlack) * inv_sc;
           l_b *= alpha;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= alpha;
