@@ -291,47 +291,52 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
   const size_t slot_elems = (size_t)a.slot_rows * DP;
   typedef typename CacheElem<FP8>::type CT;
   const CT* cache_o = (const CT*)a.cache_o;
-  for (int e = nf; e < nf + nr; ++e) {
-    const int slot = ent[2 * (e0 + e) + 1];
-    const size_t slot_base = (size_t)bh * a.num_slots + slot;
-    const float lse2 = a.cache_lse[slot_base * a.slot_rows + myrow] * kLog2e;
-    const CT* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
-    if constexpr (FP8) {
-      u32x4 raw8[NDT];
+  // The reused states are taken RB at a time: their loads are all issued before the first
+  // of them is folded, so a wave waits for one memory round trip per RB states.
+  constexpr int RB = 4;
+  constexpr int NW = FP8 ? 1 : 2;               // 16-byte words per lane per d tile
+  for (int e = nf; e < nf + nr; e += RB) {
+    u32x4 raw[RB][NDT][NW];
+    float lse2[RB];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) raw8[dt] = ld16(src + dt * 1024 + lane * 16);
-      const float mn = fmaxf(m_row, lse2);
-      const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
+    for (int q = 0; q < RB; ++q) {
+      if (e + q < nf + nr) {                      // wave-uniform
+        const int slot = ent[2 * (e0 + e + q) + 1];
+        const size_t slot_base = (size_t)bh * a.num_slots + slot;
+        lse2[q] = a.cache_lse[slot_base * a.slot_rows + myrow];
+        const CT* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        float v[16];
-        fp8_unpack16(raw8[dt], v);
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] = acc[dt][r] * fa + v[r] * fb;
-      }
-      l_row = l_row * fa + fb;
-      m_row = mn;
-      continue;
-    }
-    u32x4 raw[NDT][2];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      raw[dt][0] = ld16(src + dt * 1024 + lane * 16);
-      raw[dt][1] = ld16(src + dt * 1024 + lane * 16 + 8);
-    }
-    const float mn = fmaxf(m_row, lse2);
-    const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x8 lo = as_bf16x8(raw[dt][0]), hi = as_bf16x8(raw[dt][1]);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        acc[dt][r] = acc[dt][r] * fa + (float)lo[r] * fb;
-        acc[dt][r + 8] = acc[dt][r + 8] * fa + (float)hi[r] * fb;
+          for (int w = 0; w < NW; ++w) raw[q][dt][w] = ld16(src + dt * 1024 + lane * 16 + w * 8);
       }
     }
-    l_row = l_row * fa + fb;
-    m_row = mn;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      if (e + q < nf + nr) {
+        const float l2 = lse2[q] * kLog2e;
+        const float mn = fmaxf(m_row, l2);
+        const float fa = fast_exp2(m_row - mn), fb = fast_exp2(l2 - mn);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          float v[16];
+          if constexpr (FP8) {
+            fp8_unpack16(raw[q][dt][0], v);
+          } else {
+            const bf16x8 lo = as_bf16x8(raw[q][dt][0]), hi = as_bf16x8(raw[q][dt][NW - 1]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              v[r] = (float)lo[r];
+              v[r + 8] = (float)hi[r];
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] = acc[dt][r] * fa + v[r] * fb;
+        }
+        l_row = l_row * fa + fb;
+        m_row = mn;
+      }
+    }
   }
   const size_t bhN = (size_t)bh * a.N;
   if (myrow < n_i) {
