@@ -38,7 +38,12 @@ from workloads.gen import head_steps_packed, head_steps  # noqa: E402
 METRIC = "dense-equiv attention TFLOP/s + ms/step, % of MFMA+HBM roofline, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
-KERNEL_NAME = "step_bf16<64, false>"
+def kernel_label(head_dim, planner, fp8):
+    """Name of the step kernel instantiation a run launches: <padded head dim, planner
+    measurement compiled in (steady planner steps; anchors launch the plain one), fp8 cache>."""
+    dp = 64 if head_dim <= 64 else (96 if head_dim <= 96 else 128)
+    meas = "true" if planner else "false"
+    return f"step_bf16<{dp}, {meas}, {'true' if fp8 else 'false'}>"
 
 
 def _gen_job(args):
@@ -78,16 +83,18 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(digest):
+def measured_traffic(digest, kernel, workload):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs,
-    only if they were taken on the current kernel source (else None)."""
+    only if they were taken on the current kernel source, the same kernel instantiation and
+    the same workload and launch mix (else None)."""
     path = os.path.join(ROOT, "profiles", "step_bf16_traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_digest") != digest:
+    if t.get("kernel_source_digest") != digest or t.get("kernel") != kernel or \
+            not str(t.get("workload", "")).startswith(workload):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -250,7 +257,10 @@ def main():
     avg_kernel_ms = kern_ms / max(launches, 1)
     achieved = fresh_flops / launches / (avg_kernel_ms * 1e-3) / 1e12
     digest = kernel_source_digest()
-    traffic = measured_traffic(digest)
+    label = kernel_label(D, args.policy == "planner", cfg.cache_dtype == "fp8")
+    # the counter run covers the fixed schedule without merging (the same launch mix)
+    traffic = measured_traffic(digest, label, cfg.name) \
+        if args.policy == "schedule" and not merge_sizes else None
     t_roof_sum = sum(w[0] / (PEAK_BF16_TFLOPS * 1e12) + (w[1] + w[2]) / (PEAK_HBM_GBS * 1e9)
                      for w in work)
     t_roof_max = sum(max(w[0] / (PEAK_BF16_TFLOPS * 1e12), (w[1] + w[2]) / (PEAK_HBM_GBS * 1e9))
@@ -277,7 +287,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": KERNEL_NAME,
+                     "traffic": traffic, "kernel": label,
                      "avg_launch_ms": round(avg_kernel_ms, 4),
                      "fresh_tflop_per_launch": round(fresh_flops / launches / 1e12, 4),
                      "kernel_source_digest": digest},
