@@ -26,7 +26,9 @@
  *     memory: the caller provides one buffer of dita_cache_required_bytes bytes, which
  *     holds the state cache, the per-step work lists, a transposed-V scratch and the
  *     device counters.  The caller owns all device memory and the stream and keeps them
- *     alive until the stream has passed the step.
+ *     alive until the stream has passed the step.  A handle allocates pinned host memory
+ *     of its own (plan uploads, the planner's read-back, merge jobs), released by
+ *     dita_cache_free.
  *   - Q, K, V and out are contiguous [B, H, N, D] (row-major, D fastest).
  *   - A handle is not thread-safe; different handles are independent.
  */
@@ -211,9 +213,11 @@ dita_status dita_get_block_plan(const dita_cache* cache, uint8_t* mask, int32_t*
                                 int32_t* counts);
 
 /* Run one denoising step's attention on `hip_stream` (a hipStream_t; NULL = default).
- *   q, k, v   device, [B,H,N,D] of qkv_dtype (bf16: |v| <= 65504, see device_v_range_errors)
- *   out       device, [B,H,N,D] f32: the merged output
- *   lse_out   device, [B,H,N] f32 natural-log L, or NULL
+ *   q, k, v   device, [B,H,N,D] of qkv_dtype (bf16: |v| <= 65504, see device_v_range_errors),
+ *             16-byte aligned
+ *   out       device, [B,H,N,D] f32: the merged output; 16-byte aligned, overlapping
+ *             neither q, k, v nor the cache buffer
+ *   lse_out   device, [B,H,N] f32 natural-log L, or NULL; 4-byte aligned
  * Fresh blocks are recomputed and written back to their slots; reused blocks are read from
  * theirs.  Stream-asynchronous: returns after enqueueing.  On success the pending policy is
  * consumed, written slots become valid and the step counter advances.
