@@ -73,7 +73,7 @@ class StepStats(ctypes.Structure):
                 ("last_cache_write_bytes", ctypes.c_double),
                 ("device_v_range_errors", ctypes.c_uint64),
                 ("profiled_steps", ctypes.c_uint64), ("step_kernel_ms", ctypes.c_double),
-                ("prep_kernel_ms", ctypes.c_double)]
+                ("prep_kernel_ms", ctypes.c_double), ("device_ref_recomputes", ctypes.c_uint64)]
 
 
 _P = ctypes.c_void_p
@@ -356,7 +356,8 @@ class Cache:
                 "last_cache_write_bytes": s.last_cache_write_bytes,
                 "device_v_range_errors": s.device_v_range_errors,
                 "profiled_steps": s.profiled_steps, "step_kernel_ms": s.step_kernel_ms,
-                "prep_kernel_ms": s.prep_kernel_ms}
+                "prep_kernel_ms": s.prep_kernel_ms,
+                "device_ref_recomputes": s.device_ref_recomputes}
 
 
 def policy_from(p) -> BlockPolicy:

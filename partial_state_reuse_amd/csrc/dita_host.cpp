@@ -324,6 +324,7 @@ dita_status eval_policy(const Geo& g, const dita_block_policy* pol, const uint8_
 struct Plan {
   bool planner_w = false;        // measure the importance after the step (anchor)
   bool planner_delta = false;    // measure the diagonal states' change during the step
+  bool all_prior = false;        // every fresh block's slot holds a state from an earlier step
   std::vector<uint8_t> mask;
   std::vector<uint8_t> key;      // mask with covered members of merged groups marked 3
   std::vector<int32_t> fresh_ptr, fresh_cols, reuse_ptr, reuse_cols;
@@ -332,7 +333,9 @@ struct Plan {
 
 // Row lists of a mask.  `covered` (P*P, may be null) marks members of merged groups whose
 // state is held by another slot: a REUSE of them reads that slot once, so they get no entry.
-void build_lists(int P, const std::vector<uint8_t>& M, const uint8_t* covered, Plan* p) {
+// `valid` (P*P, may be null = none) marks slots holding a state from an earlier step.
+void build_lists(int P, const std::vector<uint8_t>& M, const uint8_t* covered,
+                 const uint8_t* valid, Plan* p) {
   p->mask = M;
   p->key = M;
   p->fresh_ptr.assign(1, 0);
@@ -340,12 +343,16 @@ void build_lists(int P, const std::vector<uint8_t>& M, const uint8_t* covered, P
   p->fresh_cols.clear();
   p->reuse_cols.clear();
   p->counts = {0, 0, 0};
+  p->all_prior = true;
   for (int i = 0; i < P; ++i) {
     for (int j = 0; j < P; ++j) {
       const size_t b = (size_t)i * P + j;
       const uint8_t m = M[b];
       p->counts[m]++;
-      if (m == DITA_FRESH) p->fresh_cols.push_back(j);
+      if (m == DITA_FRESH) {
+        p->fresh_cols.push_back(j);
+        if (!valid || !valid[b]) p->all_prior = false;
+      }
       if (m == DITA_REUSE) {
         if (covered && covered[b]) p->key[b] = 3;
         else p->reuse_cols.push_back(j);
@@ -557,6 +564,8 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->delta_part = nullptr;
   a->delta_stride = g.slot_rows / 32;
   a->cache_fp8 = g.cache_o == DITA_FP8_E4M3 ? 1 : 0;
+  a->fixed_ref = 0;
+  a->fixup = 0;
 }
 
 dita_status hip_check(hipError_t e, const char* what) {
@@ -858,7 +867,7 @@ dita_status dita_set_block_policy(dita_cache* c, const dita_block_policy* policy
         return fail(DITA_ERR_POLICY, "block (%d,%d) is merged with (%d,%d): a merged group is "
                     "reused or recomputed as a whole", i, j, i, c->head[b]);
     }
-  build_lists(c->g.P, M, covered.data(), &c->pending);
+  build_lists(c->g.P, M, covered.data(), c->valid.data(), &c->pending);
   c->pending.planner_w = meas_w;
   c->pending.planner_delta = meas_delta;
   c->has_pending = true;
@@ -917,6 +926,7 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
     }
   }
   if (c->pending.planner_delta) a.delta_part = (float*)(c->dev + c->L.delta);
+  a.fixed_ref = c->pending.all_prior ? 1 : 0;
   TimedStep* ts = nullptr;
   if (c->profiling) {
     ts = &c->timing[c->timing_next];
@@ -1167,7 +1177,7 @@ dita_status dita_get_stats(const dita_cache* cc, dita_step_stats* s) {
   s->step_kernel_ms = c->step_ms;
   s->prep_kernel_ms = c->prep_ms;
   if (c->dev_init) {
-    unsigned long long cnt[3] = {0, 0, 0};
+    unsigned long long cnt[4] = {0, 0, 0, 0};
     dita_status st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
     if (st) return st;
     st = hip_check(hipMemcpy(cnt, c->dev + c->L.counters, sizeof cnt, hipMemcpyDeviceToHost),
@@ -1176,6 +1186,7 @@ dita_status dita_get_stats(const dita_cache* cc, dita_step_stats* s) {
     s->device_fresh_blocks = cnt[0];
     s->device_reuse_blocks = cnt[1];
     s->device_v_range_errors = cnt[2];
+    s->device_ref_recomputes = cnt[3];
   }
   return ok();
 }

@@ -58,7 +58,9 @@ struct StepArgs {
                              // f32:  [B*H][slots][DP][slot_rows]
   float* cache_lse;          // [B*H][slots][slot_rows], natural log
   unsigned long long* counters;  // [0] fresh blocks, [1] reused blocks, [2] V elements
-                                 // outside the fp16 range (cumulative)
+                                 // outside the fp16 range, [3] steps computed a second time
+                                 // (cumulative); [4] this step's fixed-reference rejection
+                                 // flag (cleared by transpose_v)
   const int32_t* plan;       // device plan (layout above)
   int32_t off_offs, off_poffs, off_tiles, off_tail, off_rows, off_ent;
   int32_t B, H, N, D, DP, P;
@@ -73,6 +75,11 @@ struct StepArgs {
   float* delta_part;
   int32_t delta_stride;      // slot_rows / 32
   int32_t cache_fp8;         // bf16 path: cached O as fp8 e4m3 (1) or bf16 (0)
+  // bf16 path: every fresh block's slot holds a state from an earlier step, so the step runs
+  // as a fixed-reference pass followed by the running-maximum kernel as a conditional second
+  // pass (fixup = 1), which exits at once unless the first pass rejected a reference
+  int32_t fixed_ref;
+  int32_t fixup;
 };
 
 hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s);

@@ -111,6 +111,7 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
   __shared__ uint16_t tile[64][129];   // 64 keys x up to 128 dims of fp16 (+1 against conflicts)
   const int bh = blockIdx.y;
   const int col0 = blockIdx.x * 64;    // padded key index
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.counters[4] = 0;
   const int* poffs = a.plan + a.off_poffs;
   const int* offs = a.plan + a.off_offs;
   // partition of this 64-key chunk (poffs are multiples of 64)
@@ -169,6 +170,17 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
 // exceeds it by more than this many powers of two, so p = 2^(s - m) stays <= 2^8 and the
 // accumulator is rescaled rarely (the result is exact either way: m is only a reference).
 constexpr float kRescaleSlack = 8.0f;
+// Fixed reference (FIXED instantiation, launched when every fresh block's slot holds its state
+// from an earlier step): each row takes that state's lse (base 2) minus kRefHeadroom as its
+// reference for the whole block, with no running maximum; consecutive steps' inputs differ
+// little, so the row sum lands near 2^kRefHeadroom.  A row sum outside [kRefLo, kRefHi] (some
+// p above 2^15, which fp16 cannot be trusted to hold, or the block's mass more than 6 powers
+// of two below the reference, where fp16 loses its small p) rejects the pass: it raises the
+// step's flag, and the running-maximum kernel, launched after it as a conditional second
+// pass, computes the whole step again.
+constexpr float kRefHeadroom = 8.0f;
+constexpr float kRefLo = 4.0f;
+constexpr float kRefHi = 32768.0f;
 
 // Wave-wide sum (every lane gets the total), in a fixed butterfly order.
 __device__ __forceinline__ float wave_sum(float x) {
@@ -358,7 +370,7 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
       a.lse_out[bhN + o_i + myrow] = (m_row + fast_log2(l_row)) * kLn2;
   }
   // block counts, once per partition row: by the wave that holds its first rows
-  if (row0 == 0 && lane == 0) {
+  if (row0 == 0 && lane == 0 && !a.fixup) {
     atomicAdd(&a.counters[0], (unsigned long long)nf);
     atomicAdd(&a.counters[1], (unsigned long long)nr);
   }
@@ -489,7 +501,8 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
 // MEASURE: the planner's measurement of the diagonal states' change is compiled in (a
 // separate instantiation, so that steps without it keep the leaner register allocation).
 // FP8: the cached O is fp8 e4m3 instead of bf16.
-template <int DP, bool MEASURE, bool FP8>
+// FIXED: the fixed-reference pass (row groups only; tail waves keep the running maximum).
+template <int DP, bool MEASURE, bool FP8, bool FIXED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 3 : 1))) void step_bf16(StepArgs a) {
   constexpr int NKC = DP / 16;        // 16-wide d chunks of Q K^T
   constexpr int NDT = DP / 32;        // 32-row d tiles of O^T
@@ -505,6 +518,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h32 = lane >> 5, l32 = lane & 31;
+  if (!FIXED && a.fixup) {                      // the conditional second pass
+    if (a.counters[4] == 0) return;
+    if (blockIdx.x == 0 && tid == 0) atomicAdd(&a.counters[3], 1ull);
+  }
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / a.num_tiles, tix = wg - bh * a.num_tiles;
   const cint* plan = as_const(a.plan);
@@ -563,7 +580,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     f32x16 bacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) bacc[dt] = (f32x16){};
-    float m_b = kNegInf, l_b = 0.f;   // l_b: this lane's partial sum (16 of the 32 keys)
+    // reference: the cached lse (fixed) or the running maximum
+    float m_b = FIXED && live
+        ? a.cache_lse[((size_t)bh * a.num_slots + slot) * a.slot_rows + myrow] * kLog2e - kRefHeadroom
+        : kNegInf;
+    float l_b = 0.f;                  // this lane's partial sum (16 of the 32 keys)
     float thr = kNegInf;              // rescale threshold: (m_b + slack) / (tau log2 e)
 
     u32x4 pk[CHK], pv[CHV];
@@ -618,19 +639,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
             if (key >= n_j) s[r] = kNegInf;
           }
         }
-        // this lane's max over its 16 keys against the rescale threshold (in score units);
-        // the query's exact max over both lanes is formed only when a rescale is due
-        float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+        if constexpr (!FIXED) {
+          // this lane's max over its 16 keys against the rescale threshold (in score units);
+          // the query's exact max over both lanes is formed only when a rescale is due
+          float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-        for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1 < 16 ? r + 1 : r]);
-        if (__any(mx > thr)) {
-          const float m_new = fmaxf(m_b, max_halves(mx, paddr) * sc);
-          const float alpha = fast_exp2(m_b - m_new);
-          m_b = m_new;
-          thr = (m_new + kRescaleSlack) * inv_sc;
-          l_b *= alpha;
+          for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1 < 16 ? r + 1 : r]);
+          if (__any(mx > thr)) {
+            const float m_new = fmaxf(m_b, max_halves(mx, paddr) * sc);
+            const float alpha = fast_exp2(m_b - m_new);
+            m_b = m_new;
+            thr = (m_new + kRescaleSlack) * inv_sc;
+            l_b *= alpha;
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= alpha;
+            for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= alpha;
+          }
         }
         f16x8 pf[2];
 #pragma unroll
@@ -655,6 +678,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
       }
     }
     if (!live) continue;
+    if constexpr (FIXED) {
+      const float lsum = sum_halves(l_b, paddr);
+      if (__any(myrow < n_i && !(lsum >= kRefLo && lsum <= kRefHi)) && lane == 0)
+        atomicOr(&a.counters[4], 1ull);
+    }
 
     block_end<NDT, MEASURE, FP8>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
                    cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
@@ -1025,15 +1053,24 @@ hipError_t launch_transpose_v(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s) {
-  const int G = a.num_tiles * a.B * a.H;
+hipError_t launch_step_bf16(const StepArgs& args, hipStream_t s) {
+  const int G = args.num_tiles * args.B * args.H;
+  StepArgs a = args;
+  a.fixup = 0;
+  // the fixed-reference pass never measures (a second pass would see its writes)
   const int m = a.delta_part != nullptr ? 1 : 0, f = a.cache_fp8 ? 2 : 0;
-#define DITA_LAUNCH_BF16(DPV)                                                                   \
-  switch (m | f) {                                                                              \
-    case 0: hipLaunchKernelGGL((step_bf16<DPV, false, false>), dim3(G), dim3(256), 0, s, a); break; \
-    case 1: hipLaunchKernelGGL((step_bf16<DPV, true, false>), dim3(G), dim3(256), 0, s, a); break;  \
-    case 2: hipLaunchKernelGGL((step_bf16<DPV, false, true>), dim3(G), dim3(256), 0, s, a); break;  \
-    default: hipLaunchKernelGGL((step_bf16<DPV, true, true>), dim3(G), dim3(256), 0, s, a); break;  \
+  const bool fixed = a.fixed_ref && !m;
+#define DITA_LAUNCH_BF16(DPV)                                                                    \
+  if (fixed) {                                                                                   \
+    if (f) hipLaunchKernelGGL((step_bf16<DPV, false, true, true>), dim3(G), dim3(256), 0, s, a);  \
+    else hipLaunchKernelGGL((step_bf16<DPV, false, false, true>), dim3(G), dim3(256), 0, s, a);   \
+    a.fixup = 1;                                                                                 \
+  }                                                                                              \
+  switch (m | f) {                                                                               \
+    case 0: hipLaunchKernelGGL((step_bf16<DPV, false, false, false>), dim3(G), dim3(256), 0, s, a); break; \
+    case 1: hipLaunchKernelGGL((step_bf16<DPV, true, false, false>), dim3(G), dim3(256), 0, s, a); break;  \
+    case 2: hipLaunchKernelGGL((step_bf16<DPV, false, true, false>), dim3(G), dim3(256), 0, s, a); break;  \
+    default: hipLaunchKernelGGL((step_bf16<DPV, true, true, false>), dim3(G), dim3(256), 0, s, a); break;  \
   }
   switch (a.DP) {
     case 64: DITA_LAUNCH_BF16(64) break;

@@ -38,14 +38,21 @@ def active_for(cfg):
 
 
 def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offsets=None,
-                  check_slots=True):
-    """Run every step on the GPU and compare with the oracle on `heads` (and `rows`)."""
+                  check_slots=True, modify=None, recomputes=None):
+    """Run every step on the GPU and compare with the oracle on `heads` (and `rows`).
+
+    modify      optional callable(dev, kept) that edits the device inputs and the host copies
+                of `heads` alike before the run
+    recomputes  None, 0 (no fresh block may be computed a second time after its cached lse
+                was rejected as the softmax reference) or "some" (at least one must be)"""
     oracle = oracle_mod()
     S = steps or cfg.steps
     bf = cfg.qkv_dtype == "bf16"
     log(f"case {cfg.name} B={cfg.batch} H={cfg.heads} N={cfg.tokens} D={cfg.head_dim} "
         f"P={cfg.num_partitions} steps={S} heads={heads} rows={'all' if rows is None else len(rows)}")
     dev, kept = gh.device_inputs(cfg, S, keep_heads=set(heads))
+    if modify is not None:
+        modify(dev, kept)
     g = dita.geometry_from(cfg, offsets=offsets)
     cache = dita.Cache(g, active_mask=active_for(cfg) if offsets is None else None)
     pols = policies or [cfg.policy(s) for s in range(1, S + 1)]
@@ -115,7 +122,12 @@ def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offset
     assert st["device_reuse_blocks"] == st["host_reuse_blocks"]
     assert st["device_v_range_errors"] == 0
     assert st["host_fresh_blocks"] == bh * sum(int(p["counts"][1]) for p in plans)
-    log(f"case {cfg.name}: worst max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e}")
+    if recomputes == 0:
+        assert st["device_ref_recomputes"] == 0, st["device_ref_recomputes"]
+    elif recomputes == "some":
+        assert st["device_ref_recomputes"] > 0
+    log(f"case {cfg.name}: worst max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e}; "
+        f"blocks recomputed after a rejected reference: {st['device_ref_recomputes']}")
     assert ok_all
     cache.free()
     return outs
@@ -180,6 +192,38 @@ def test_explicit_masks_and_custom_offsets_bf16(dita):
                         grid_h=10, grid_w=10, num_partitions=P, steps=4, qkv_dtype="bf16",
                         cache_dtype="bf16")
     run_and_check(dita, cfg, heads=[(0, 0), (0, 1)], policies=masks, offsets=offs)
+
+
+def test_fixed_reference_fallback_bf16(dita):
+    """A fresh block whose slot holds an earlier state takes that state's lse as its softmax
+    reference.  Here one key partition's K is scaled by 4 on step 2 and restored on step 3,
+    so the lse of its blocks jumps up, then down, far beyond the accepted window: those
+    blocks are computed a second time with the running maximum (counted on the device),
+    and the outputs still match the oracle on the same inputs.  Two 130-row partitions
+    exercise the tail waves too."""
+    from oracle.policy import partition_offsets
+    sched = wcfg.AnchorThen(Policy(kind=wcfg.FRESH_BUDGET, reuse_percent=0))
+    cfg = custom_config(name="ref-jump", idx=47, heads=2, head_dim=64, frames=4, grid_h=10,
+                        grid_w=26, num_partitions=8, steps=3, qkv_dtype="bf16",
+                        cache_dtype="bf16", schedule=sched)
+    offs = partition_offsets(cfg.tokens, cfg.num_partitions)
+    j0, j1 = offs[3], offs[4]
+
+    def modify(dev, kept):
+        dev[1][1][:, :, j0:j1, :] *= 4                 # exact in bf16
+        for bh in kept:
+            kept[bh][1][1][j0:j1] *= 4
+    run_and_check(dita, cfg, heads=[(0, 0), (0, 1)], modify=modify, recomputes="some")
+
+
+def test_fixed_reference_smooth_drift_bf16(dita):
+    """With the seeded drift between steps every fresh block keeps its cached lse as the
+    reference: no block is computed twice."""
+    sched = wcfg.AnchorThen(Policy(kind=wcfg.FRESH_BUDGET, reuse_percent=40))
+    cfg = custom_config(name="ref-drift", idx=48, heads=2, head_dim=64, frames=4, grid_h=10,
+                        grid_w=26, num_partitions=8, steps=4, qkv_dtype="bf16",
+                        cache_dtype="bf16", schedule=sched)
+    run_and_check(dita, cfg, heads=[(0, 0), (0, 1)], recomputes=0)
 
 
 def test_f32_random_geometries(dita):
@@ -262,7 +306,7 @@ def _full(dita, idx, heads, per_part):
     cfg = CONFIGS[idx]
     rows = gh.sample_rows(partition_offsets(cfg.tokens, cfg.num_partitions), per_part,
                           np.random.default_rng(idx))
-    run_and_check(dita, cfg, heads=heads, rows=rows)
+    run_and_check(dita, cfg, heads=heads, rows=rows, recomputes=0)
 
 
 def test_full_video29f_720p(dita):
