@@ -39,11 +39,14 @@ METRIC = "dense-equiv attention TFLOP/s + ms/step, % of MFMA+HBM roofline, 1 GPU
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 def kernel_label(head_dim, planner, fp8):
-    """Name of the step kernel instantiation a run launches: <padded head dim, planner
-    measurement compiled in (steady planner steps; anchors launch the plain one), fp8 cache>."""
+    """Name of the step kernel instantiation a run's steady steps launch: <padded head dim,
+    planner measurement compiled in, fp8 cache, fixed reference>.  Fixed-schedule steps after
+    the anchor run the fixed-reference pass (followed by the running-maximum kernel as a
+    conditional second pass, which exits at once unless a reference was rejected); anchor
+    steps, and planner steps (which measure), run the running-maximum kernel."""
     dp = 64 if head_dim <= 64 else (96 if head_dim <= 96 else 128)
-    meas = "true" if planner else "false"
-    return f"step_bf16<{dp}, {meas}, {'true' if fp8 else 'false'}>"
+    t = lambda b: "true" if b else "false"
+    return f"step_bf16<{dp}, {t(planner)}, {t(fp8)}, {t(not planner)}>"
 
 
 def _gen_job(args):
@@ -84,9 +87,9 @@ def kernel_source_digest():
 
 
 def measured_traffic(digest, kernel, workload):
-    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs,
-    only if they were taken on the current kernel source, the same kernel instantiation and
-    the same workload and launch mix (else None)."""
+    """HBM bytes per step of the step kernel (every dispatch of the step summed) from
+    committed rocprofv3 counter runs, only if they were taken on the current kernel source,
+    the same kernel instantiation and the same workload and step mix (else None)."""
     path = os.path.join(ROOT, "profiles", "step_bf16_traffic.json")
     try:
         with open(path) as f:
@@ -96,7 +99,7 @@ def measured_traffic(digest, kernel, workload):
     if t.get("kernel_source_digest") != digest or t.get("kernel") != kernel or \
             not str(t.get("workload", "")).startswith(workload):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("hbm_bytes_per_step")
 
 
 def main():
@@ -253,6 +256,8 @@ def main():
     cache_bytes = sum(w[1] + w[2] for w in work)
     kern_ms = st["step_kernel_ms"]
     prep_ms = st["prep_kernel_ms"]
+    # per step: the step kernel's dispatches (after the anchor: the fixed-reference pass and the
+    # conditional second pass, which exits at once) between the library's HIP events
     launches = st["profiled_steps"]
     avg_kernel_ms = kern_ms / max(launches, 1)
     achieved = fresh_flops / launches / (avg_kernel_ms * 1e-3) / 1e12
@@ -288,8 +293,8 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": label,
-                     "avg_launch_ms": round(avg_kernel_ms, 4),
-                     "fresh_tflop_per_launch": round(fresh_flops / launches / 1e12, 4),
+                     "kernel_ms_per_step": round(avg_kernel_ms, 4),
+                     "fresh_tflop_per_step": round(fresh_flops / launches / 1e12, 4),
                      "kernel_source_digest": digest},
         "roofline_combined": {
             "t_roof_ms_per_step": round(t_roof_sum * 1e3 / K, 4),
