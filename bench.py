@@ -40,13 +40,13 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 def kernel_label(head_dim, planner, fp8):
     """Name of the step kernel instantiation a run's steady steps launch: <padded head dim,
-    planner measurement compiled in, fp8 cache, fixed reference>.  Fixed-schedule steps after
-    the anchor run the fixed-reference pass (followed by the running-maximum kernel as a
-    conditional second pass, which exits at once unless a reference was rejected); anchor
-    steps, and planner steps (which measure), run the running-maximum kernel."""
+    planner measurement compiled in, fp8 cache, fixed reference>.  Steps after the anchor run
+    the fixed-reference pass (followed by the running-maximum kernel as a conditional second
+    pass, which exits at once unless a reference was rejected); anchor steps run the
+    running-maximum kernel."""
     dp = 64 if head_dim <= 64 else (96 if head_dim <= 96 else 128)
     t = lambda b: "true" if b else "false"
-    return f"step_bf16<{dp}, {t(planner)}, {t(fp8)}, {t(not planner)}>"
+    return f"step_bf16<{dp}, {t(planner)}, {t(fp8)}, true>"
 
 
 def _gen_job(args):

@@ -365,7 +365,7 @@ void build_lists(int P, const std::vector<uint8_t>& M, const uint8_t* covered,
 
 struct Layout {
   size_t counters = 0, plans = 0, plan_bytes = 0, vt = 0, lse = 0, o = 0, delta = 0, pout = 0,
-         wpart = 0, merge = 0, merge_bytes = 0, total = 0;
+         wpart = 0, merge = 0, merge_bytes = 0, snap = 0, total = 0;
 };
 
 Layout compute_layout(const Geo& g, int num_slots) {
@@ -397,6 +397,9 @@ Layout compute_layout(const Geo& g, int num_slots) {
   L.merge = at;
   L.merge_bytes = align_up((4 * P * ((P + 1) / 2) + P * P) * 4, 256);
   at += L.merge_bytes;
+  // bf16: snapshot of the diagonal slots' cached O, taken before each measuring step
+  L.snap = at;
+  if (g.bf16()) at = align_up(at + bh * P * (size_t)g.slot_rows * g.DP * esz, 256);
   L.total = at;
   return L;
 }
@@ -566,6 +569,7 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->cache_fp8 = g.cache_o == DITA_FP8_E4M3 ? 1 : 0;
   a->fixed_ref = 0;
   a->fixup = 0;
+  a->diag_snap = nullptr;
 }
 
 dita_status hip_check(hipError_t e, const char* what) {
@@ -927,6 +931,11 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
   }
   if (c->pending.planner_delta) a.delta_part = (float*)(c->dev + c->L.delta);
   a.fixed_ref = c->pending.all_prior ? 1 : 0;
+  // a measuring bf16 step keeps the old diagonal states aside (the snapshot's grid has one
+  // row per b*h: beyond 65535 the step keeps the running maximum and measures in place)
+  const bool snap = c->g.bf16() && c->pending.planner_delta &&
+                    (int64_t)c->g.B * c->g.H <= 65535;
+  if (snap) a.diag_snap = c->dev + c->L.snap;
   TimedStep* ts = nullptr;
   if (c->profiling) {
     ts = &c->timing[c->timing_next];
@@ -941,6 +950,10 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
     if (st) return st;
   }
   if (c->g.bf16()) {
+    if (snap) {
+      st = hip_check(dita::launch_snapshot_diag(a, s), "snapshot launch");
+      if (st) return st;
+    }
     st = hip_check(dita::launch_transpose_v(a, s), "transpose launch");
     if (st) return st;
     if (ts) {

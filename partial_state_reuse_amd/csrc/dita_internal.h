@@ -74,6 +74,10 @@ struct StepArgs {
   // (new cached O - old cached O)^2 at delta_part[(bh * P + i) * delta_stride + row / 32].
   float* delta_part;
   int32_t delta_stride;      // slot_rows / 32
+  // bf16 path, measuring steps: the diagonal slots' cached O as it was before the step
+  // ([B*H][P][slot_rows/32][DP/32][64][16], as a slot), which the measurement reads as the old
+  // state, so that a second pass over the step measures the same change
+  const void* diag_snap;
   int32_t cache_fp8;         // bf16 path: cached O as fp8 e4m3 (1) or bf16 (0)
   // bf16 path: every fresh block's slot holds a state from an earlier step, so the step runs
   // as a fixed-reference pass followed by the running-maximum kernel as a conditional second
@@ -95,6 +99,7 @@ hipError_t launch_step_f32(const StepArgs& a, hipStream_t s);
 // (P * planner_chunks(P) * P floats), then one sum per partition.
 inline int planner_chunks(int P) { return P >= 2048 ? 1 : (2048 / P > 64 ? 64 : 2048 / P); }
 hipError_t launch_planner_delta(const StepArgs& a, float* delta, hipStream_t s);
+hipError_t launch_snapshot_diag(const StepArgs& a, hipStream_t s);
 hipError_t launch_planner_weights(const StepArgs& a, float* w, float* part, hipStream_t s);
 // Group composition: job k = jobs[4k..4k+3] = {n_i, dst slot, first source, sources}; the
 // sources are slot numbers in srcs.  Grid (njobs, slot_rows / 32 sub-tiles, B*H).

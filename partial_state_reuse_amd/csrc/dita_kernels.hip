@@ -229,11 +229,17 @@ __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT]
                                           f32x16 (&acc)[NDT],
                                           float& m_row, float& l_row, bool diag, int n_i,
                                           int i, int bh) {
+  typedef typename CacheElem<FP8>::type CT;
   const int lane = threadIdx.x & 63, h32 = lane >> 5;
   const float lsum = sum_halves(l_b, paddr);
   const float inv = 1.0f / lsum;
   const float lse2 = m_b + fast_log2(lsum);      // block lse, base 2
   const bool measure = MEASURE && diag;                    // wave-uniform
+  // the old state: the step's snapshot of the diagonal slots, else the slot itself
+  const CT* old = MEASURE && a.diag_snap
+      ? (const CT*)a.diag_snap + ((size_t)bh * a.P + i) * ((size_t)a.slot_rows * NDT * 32) +
+            (size_t)row0 * NDT * 32
+      : dst;
   float sq = 0.f;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
@@ -243,7 +249,7 @@ __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT]
       if (measure) {
         float nv[16], ov[16];
         fp8_unpack16(w, nv);
-        fp8_unpack16(ld16(dst + dt * 1024 + lane * 16), ov);
+        fp8_unpack16(ld16(old + dt * 1024 + lane * 16), ov);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int d = dt * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
@@ -263,7 +269,7 @@ __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT]
       e1p[r] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][r + 8]);
     }
     if (measure) {
-      const u32x4 o0 = ld16(dst + dt * 1024 + lane * 16), o1 = ld16(dst + dt * 1024 + lane * 16 + 8);
+      const u32x4 o0 = ld16(old + dt * 1024 + lane * 16), o1 = ld16(old + dt * 1024 + lane * 16 + 8);
       const bf16x8 n0 = as_bf16x8(w0), n1 = as_bf16x8(w1), p0 = as_bf16x8(o0), p1 = as_bf16x8(o1);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -860,6 +866,25 @@ __global__ void read_slot(StepArgs a, int bh, int slot, int n_i, float* o_out, f
 // planner reductions (one workgroup per query partition i, fixed summation order)
 // ------------------------------------------------------------------------------------------
 // Sum of 256 per-thread doubles, tree order fixed; the result is in red[0].
+// Snapshot of the diagonal slots' cached O before a measuring step: one workgroup per
+// (partition i, b*h) copies the slot of block (i, i) (found among row i's fresh entries:
+// the diagonal block is always fresh) in 16-byte words.
+__global__ __launch_bounds__(256) void snapshot_diag(StepArgs a, int slot_bytes) {
+  const int i = blockIdx.x, bh = blockIdx.y;
+  const cint* plan = as_const(a.plan);
+  const cint* rinfo = plan + a.off_rows + 4 * i;
+  const cint* ent = plan + a.off_ent;
+  const int e0 = rinfo[0], nf = rinfo[1];
+  int slot = -1;
+  for (int e = 0; e < nf; ++e)
+    if (ent[2 * (e0 + e)] == i) slot = ent[2 * (e0 + e) + 1];
+  if (slot < 0) return;
+  const u32x4* src = (const u32x4*)((const uint8_t*)a.cache_o +
+                                    ((size_t)bh * a.num_slots + slot) * (size_t)slot_bytes);
+  u32x4* dst = (u32x4*)((uint8_t*)a.diag_snap + ((size_t)bh * a.P + i) * (size_t)slot_bytes);
+  for (int w = threadIdx.x; w < slot_bytes / 16; w += 256) dst[w] = src[w];
+}
+
 __device__ __forceinline__ void block_sum(double* red, double x) {
   red[threadIdx.x] = x;
   __syncthreads();
@@ -1057,13 +1082,18 @@ hipError_t launch_step_bf16(const StepArgs& args, hipStream_t s) {
   const int G = args.num_tiles * args.B * args.H;
   StepArgs a = args;
   a.fixup = 0;
-  // the fixed-reference pass never measures (a second pass would see its writes)
+  // a measuring step takes the fixed-reference pass only with the snapshot of the old diagonal
+  // states (a second pass would otherwise measure against the first pass's writes)
   const int m = a.delta_part != nullptr ? 1 : 0, f = a.cache_fp8 ? 2 : 0;
-  const bool fixed = a.fixed_ref && !m;
+  const bool fixed = a.fixed_ref && (!m || a.diag_snap);
 #define DITA_LAUNCH_BF16(DPV)                                                                    \
   if (fixed) {                                                                                   \
-    if (f) hipLaunchKernelGGL((step_bf16<DPV, false, true, true>), dim3(G), dim3(256), 0, s, a);  \
-    else hipLaunchKernelGGL((step_bf16<DPV, false, false, true>), dim3(G), dim3(256), 0, s, a);   \
+    switch (m | f) {                                                                             \
+      case 0: hipLaunchKernelGGL((step_bf16<DPV, false, false, true>), dim3(G), dim3(256), 0, s, a); break; \
+      case 1: hipLaunchKernelGGL((step_bf16<DPV, true, false, true>), dim3(G), dim3(256), 0, s, a); break;  \
+      case 2: hipLaunchKernelGGL((step_bf16<DPV, false, true, true>), dim3(G), dim3(256), 0, s, a); break;  \
+      default: hipLaunchKernelGGL((step_bf16<DPV, true, true, true>), dim3(G), dim3(256), 0, s, a); break;  \
+    }                                                                                            \
     a.fixup = 1;                                                                                 \
   }                                                                                              \
   switch (m | f) {                                                                               \
@@ -1085,6 +1115,12 @@ hipError_t launch_step_bf16(const StepArgs& args, hipStream_t s) {
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t s) {
   const int G = a.num_tiles * a.B * a.H;
   hipLaunchKernelGGL(step_f32, dim3(G), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_snapshot_diag(const StepArgs& a, hipStream_t s) {
+  const int slot_bytes = a.slot_rows * a.DP * (a.cache_fp8 ? 1 : 2);
+  hipLaunchKernelGGL(snapshot_diag, dim3(a.P, a.B * a.H), dim3(256), 0, s, a, slot_bytes);
   return hipGetLastError();
 }
 

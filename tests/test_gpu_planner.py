@@ -49,6 +49,30 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_planner_schedule(dita, case):
+    run_planner_case(dita, case)
+
+
+def test_planner_measures_through_a_second_pass(dita):
+    """Steps after the anchor run the fixed-reference pass, which measures the growth against
+    a snapshot of the old diagonal states (in its 128-row groups; tail waves keep the running
+    maximum, so the partitions here hold 130 rows).  One key partition's K scaled by 8 on
+    step 3 (and restored on step 4) makes the pass reject its reference on both steps: the
+    second pass
+    computes them again, measuring the same change, and decisions, measurements and outputs
+    still match the oracle on the same inputs."""
+    from oracle.policy import partition_offsets
+    case = ("planner-lse-jump", 4, 10, 26, 8, 64, 2, 6, "bf16", 60, 1, 0, 0.0, False)
+    offs = partition_offsets(4 * 10 * 26, 8)
+    j0, j1 = offs[2], offs[3]
+
+    def modify(dev, kept):
+        dev[2][1][:, :, j0:j1, :] *= 8                 # exact in bf16
+        for bh in kept:
+            kept[bh][2][1][j0:j1] *= 8
+    run_planner_case(dita, case, modify=modify, recomputes="some")
+
+
+def run_planner_case(dita, case, modify=None, recomputes=None):
     import oracle
     from oracle.policy import active_mask, partition_offsets, FRESH, SKIP
     name, T, gh_, gw, P, D, H, S, dt, pct, G, period, cap, tile = case
@@ -63,6 +87,8 @@ def test_planner_schedule(dita, case):
     log(f"case {name}: N={cfg.tokens} P={P} D={D} H={H} steps={S} {dt} reuse={pct}% G={G} "
         f"period={period} cap={cap} tile={tile}")
     dev, kept = gh.device_inputs(cfg, S, keep_heads=set(heads))
+    if modify is not None:
+        modify(dev, kept)
     cache = dita.Cache(dita.geometry_from(cfg), active_mask=act.astype(np.uint8))
     masks, outs, states = [], [], []
     for s in range(S):
@@ -72,7 +98,13 @@ def test_planner_schedule(dita, case):
         out, _ = cache.step(q, k, v)
         outs.append(out.cpu().numpy())
         states.append(cache.planner_state())
+    recomputed = cache.stats()["device_ref_recomputes"]
     cache.free()
+    log(f"steps computed a second time: {recomputed}")
+    if recomputes == "some":
+        assert recomputed > 0
+    elif recomputes == 0:
+        assert recomputed == 0
 
     # decisions, bit for bit
     n_reuse_steps = 0
