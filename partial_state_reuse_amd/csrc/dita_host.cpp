@@ -57,7 +57,7 @@ struct Geo {
   int num_tiles = 0;                 // workgroups per (b, h): tail workgroups, then groups
   int num_tail_wg = 0;               // tail workgroups per (b, h)
   std::vector<int32_t> groups;       // per partition: row groups run by 4-wave workgroups
-  std::vector<int32_t> tails;        // {i, first row} per tail sub-tile, padded to 4 per wg
+  std::vector<int32_t> tails;        // {i, first row} per tail sub-tile (one per workgroup)
   int slot_rows = 0;
   bool bf16() const { return qkv == DITA_BF16; }
   // bytes per cached O element
@@ -129,8 +129,8 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
     r.frame[p] = (int32_t)(r.c2[p] / (2 * (int64_t)r.F));
     r.poffs[p + 1] = r.poffs[p] + (int)align_up(n, dita::kKeyTile);
     // Row groups of wg_rows rows.  On the bf16 path a last group that would keep at most
-    // kMaxTailSubtiles of its 4 waves busy becomes tail sub-tiles instead: they run as
-    // independent waves, 4 to a workgroup, so no wave slot idles on an empty sub-tile.
+    // kMaxTailSubtiles of its 4 waves busy becomes tail sub-tiles instead: one workgroup per
+    // sub-tile, whose 4 waves share the row's blocks, so no wave slot idles on empty rows.
     int full = n / r.wg_rows;
     const int rem = n - full * r.wg_rows;
     const int sub = (rem + 31) / 32;
@@ -145,11 +145,7 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
     r.groups[p] = full;
     num_groups += full;
   }
-  while (r.tails.size() % 8) {
-    r.tails.push_back(-1);
-    r.tails.push_back(0);
-  }
-  r.num_tail_wg = (int)(r.tails.size() / 8);
+  r.num_tail_wg = (int)(r.tails.size() / 2);
   r.num_tiles = r.num_tail_wg + num_groups;
   r.kt_pad = r.poffs[r.P];
   r.slot_rows = (int)align_up(max_n, dita::kSlotRowAlign);
@@ -372,7 +368,7 @@ Layout compute_layout(const Geo& g, int num_slots) {
   Layout L;
   const size_t P = g.P;
   const size_t words =
-      dita::kPlanHeader + 2 * (P + 1) + g.num_tiles + 8 * g.num_tail_wg + 4 * P + 2 * P * P;
+      dita::kPlanHeader + 2 * (P + 1) + g.num_tiles + 2 * g.num_tail_wg + 4 * P + 2 * P * P;
   L.counters = 0;
   L.plans = 256;
   L.plan_bytes = align_up(words * 4, 256);
@@ -556,7 +552,7 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->off_poffs = a->off_offs + P + 1;
   a->off_tiles = a->off_poffs + P + 1;
   a->off_tail = a->off_tiles + g.num_tiles;
-  a->off_rows = a->off_tail + 8 * g.num_tail_wg;
+  a->off_rows = a->off_tail + 2 * g.num_tail_wg;
   a->off_ent = a->off_rows + 4 * P;
   a->B = g.B; a->H = g.H; a->N = g.N; a->D = g.D; a->DP = g.DP; a->P = P;
   a->num_tiles = g.num_tiles;

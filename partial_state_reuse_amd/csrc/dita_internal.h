@@ -34,16 +34,16 @@ inline int bf16_wg_rows(int /*DP*/) { return kWaves * 32; }
 //   tiles  at kPlanHeader + 2(P+1)        : num_tiles words: (i << 16) | group-in-partition
 //                                           for a workgroup of 4 waves on consecutive rows,
 //                                           or kTailFlag | k for tail workgroup k
-//   tails  at tiles + num_tiles           : 8 words per tail workgroup: {i, first row} of the
-//                                           32-row sub-tile each of its 4 waves owns ({-1, 0}:
-//                                           none)
-//   rows   at tails + 8 * tail workgroups : P x 4 words {first entry, #fresh, #reuse, 0}
+//   tails  at tiles + num_tiles           : 2 words per tail workgroup: {i, first row} of
+//                                           its 32-row sub-tile
+//   rows   at tails + 2 * tail workgroups : P x 4 words {first entry, #fresh, #reuse, 0}
 //   ent    at rows + 4P                   : E x 2 words {j, slot}; per row the fresh blocks
 //                                           (ascending j) precede the reused ones
 constexpr int kPlanHeader = 4;
 constexpr int32_t kTailFlag = 1 << 30;
 // bf16 path: a partition whose last row group would leave at most this many of its 4 waves
-// with rows hands those rows to tail workgroups instead (sub-tiles packed 4 per workgroup).
+// with rows hands those rows to tail workgroups instead (one workgroup per 32-row sub-tile,
+// its 4 waves sharing the row's blocks).
 constexpr int kMaxTailSubtiles = 2;
 
 struct StepArgs {

@@ -295,13 +295,12 @@ __device__ __forceinline__ void block_end(const StepArgs& a, f32x16 (&bacc)[NDT]
   m_row = mn;
 }
 
-// Reused blocks folded into the row's merge, then the epilogue (out = acc / l, lse) and the
-// per-partition block counts, for the wave's 32-row sub-tile.
-template <int DP, bool FP8>
-__device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int i, int o_i,
-                                                 int n_i, int row0, int e0, int nf, int nr,
-                                                 f32x16 (&acc)[DP / 32], float m_row,
-                                                 float l_row) {
+// Reused states e_begin, e_begin + STEP, ... (below e_end) folded into the row's merge, for
+// the wave's 32-row sub-tile.
+template <int DP, bool FP8, int STEP>
+__device__ __forceinline__ void reuse_fold(const StepArgs& a, int bh, int row0, int e0,
+                                           int e_begin, int e_end, f32x16 (&acc)[DP / 32],
+                                           float& m_row, float& l_row) {
   constexpr int NDT = DP / 32;
   const int lane = threadIdx.x & 63, h32 = lane >> 5, l32 = lane & 31;
   const int myrow = row0 + l32;
@@ -313,13 +312,13 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
   // of them is folded, so a wave waits for one memory round trip per RB states.
   constexpr int RB = 4;
   constexpr int NW = FP8 ? 1 : 2;               // 16-byte words per lane per d tile
-  for (int e = nf; e < nf + nr; e += RB) {
+  for (int e = e_begin; e < e_end; e += RB * STEP) {
     u32x4 raw[RB][NDT][NW];
     float lse2[RB];
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
-      if (e + q < nf + nr) {                      // wave-uniform
-        const int slot = ent[2 * (e0 + e + q) + 1];
+      if (e + q * STEP < e_end) {                 // wave-uniform
+        const int slot = ent[2 * (e0 + e + q * STEP) + 1];
         const size_t slot_base = (size_t)bh * a.num_slots + slot;
         lse2[q] = a.cache_lse[slot_base * a.slot_rows + myrow];
         const CT* src = cache_o + slot_base * slot_elems + (size_t)row0 * DP;
@@ -331,7 +330,7 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
     }
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
-      if (e + q < nf + nr) {
+      if (e + q * STEP < e_end) {
         const float l2 = lse2[q] * kLog2e;
         const float mn = fmaxf(m_row, l2);
         const float fa = fast_exp2(m_row - mn), fb = fast_exp2(l2 - mn);
@@ -356,6 +355,18 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
       }
     }
   }
+}
+
+// The epilogue (out = acc / l, lse) and the per-partition block counts, for the wave's
+// 32-row sub-tile.
+template <int DP>
+__device__ __forceinline__ void finish_rows(const StepArgs& a, int bh, int o_i, int n_i,
+                                            int row0, int nf, int nr,
+                                            const f32x16 (&acc)[DP / 32], float m_row,
+                                            float l_row) {
+  constexpr int NDT = DP / 32;
+  const int lane = threadIdx.x & 63, h32 = lane >> 5, l32 = lane & 31;
+  const int myrow = row0 + l32;
   const size_t bhN = (size_t)bh * a.N;
   if (myrow < n_i) {
     const float inv = 1.0f / l_row;
@@ -382,20 +393,31 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
   }
 }
 
-// Tail workgroup: 4 independent waves, each with its own 32-row sub-tile (possibly of
-// different partitions); each reads its K / V^T fragments straight from global memory (L2),
-// with no LDS and no barrier.
+// Reused blocks folded into the row's merge, then the epilogue.
+template <int DP, bool FP8>
+__device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int i, int o_i,
+                                                 int n_i, int row0, int e0, int nf, int nr,
+                                                 f32x16 (&acc)[DP / 32], float m_row,
+                                                 float l_row) {
+  reuse_fold<DP, FP8, 1>(a, bh, row0, e0, nf, nf + nr, acc, m_row, l_row);
+  finish_rows<DP>(a, bh, o_i, n_i, row0, nf, nr, acc, m_row, l_row);
+}
+
+// Tail workgroup: one 32-row sub-tile left at the end of a partition.  Its 4 waves share the
+// row's blocks: wave w computes every 4th fresh block from the w-th and folds every 4th
+// reused state, each into a partial merge of its own; the partial merges are combined through
+// LDS (the merge is exact in any order) and wave 0 writes the rows.  K / V^T fragments come
+// straight from global memory (L2).  `lds` holds at least 2 x 64 x (2 + DP / 2) floats.
 template <int DP, bool MEASURE, bool FP8>
-__device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
+__device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, float* lds) {
   constexpr int NKC = DP / 16, NDT = DP / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h32 = lane >> 5, l32 = lane & 31;
   const cint* plan = as_const(a.plan);
   const cint* offs = plan + a.off_offs;
   const cint* poffs = plan + a.off_poffs;
-  const cint* te = plan + a.off_tail + 8 * k + 2 * wave;
+  const cint* te = plan + a.off_tail + 2 * k;
   const int i = te[0], row0 = te[1];
-  if (i < 0) return;                              // no sub-tile for this wave
   const int o_i = offs[i], n_i = offs[i + 1] - o_i;
   const int myrow = row0 + l32;
   const cint* rinfo = plan + a.off_rows + 4 * i;
@@ -429,7 +451,7 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
   const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
 
   // ---------------- fresh blocks ----------------
-  for (int e = 0; e < nf; ++e) {
+  for (int e = wave; e < nf; e += kWaves) {
     const int j = ent[2 * (e0 + e)], slot = ent[2 * (e0 + e) + 1];
     const int o_j = offs[j], n_j = offs[j + 1] - o_j, po_j = poffs[j];
     f32x16 bacc[NDT];
@@ -501,7 +523,42 @@ __device__ __forceinline__ void tail_wave(const StepArgs& a, int bh, int k) {
                    cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
                    acc, m_row, l_row, j == i, n_i, i, bh);
   }
-  reuse_and_finish<DP, FP8>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
+  reuse_fold<DP, FP8, kWaves>(a, bh, row0, e0, nf + wave, nf + nr, acc, m_row, l_row);
+
+  // combine the partial merges: waves 2, 3 into 0, 1, then 1 into 0
+  constexpr int W = 2 + NDT * 16;               // floats per lane
+  auto put = [&](int slot) {
+    float* p = lds + (size_t)slot * W * 64 + lane;
+    p[0] = m_row;
+    p[64] = l_row;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[(2 + dt * 16 + r) * 64] = acc[dt][r];
+  };
+  auto take = [&](int slot) {
+    const float* p = lds + (size_t)slot * W * 64 + lane;
+    const float m2 = p[0], l2 = p[64];
+    const float mn = fmaxf(m_row, m2);
+    const float fa = m_row == kNegInf ? 0.f : fast_exp2(m_row - mn);
+    const float fb = m2 == kNegInf ? 0.f : fast_exp2(m2 - mn);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] = acc[dt][r] * fa + p[(2 + dt * 16 + r) * 64] * fb;
+    l_row = l_row * fa + l2 * fb;
+    m_row = mn;
+  };
+  if (wave >= 2) put(wave - 2);
+  __syncthreads();
+  if (wave < 2) take(wave);
+  __syncthreads();
+  if (wave == 1) put(0);
+  __syncthreads();
+  if (wave == 0) {
+    take(0);
+    finish_rows<DP>(a, bh, o_i, n_i, row0, nf, nr, acc, m_row, l_row);
+  }
 }
 
 // MEASURE: the planner's measurement of the diagonal states' change is compiled in (a
@@ -519,8 +576,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   constexpr int CHK = KT * DP / 8 / 256;   // 16-byte chunks per thread per K tile
   constexpr int CHV = DP * KT / 8 / 256;   // ... per V^T tile
   constexpr int WG_ROWS = kWaves * 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KT * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * LDV];
+  // K tile, then V^T tile; the tail workgroups use the same memory for their merge
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KT * LDK + DP * LDV];
+  uint16_t* const sK = smem;
+  uint16_t* const sV = smem + KT * LDK;
+  static_assert(sizeof(smem) >= 2 * 64 * (2 + DP / 2) * sizeof(float), "tail merge buffer");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h32 = lane >> 5, l32 = lane & 31;
@@ -535,7 +595,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const cint* poffs = plan + a.off_poffs;
   const int packed = plan[a.off_tiles + tix];
   if (packed & kTailFlag) {                     // workgroup-uniform
-    tail_wave<DP, MEASURE, FP8>(a, bh, packed & 0xffff);
+    tail_group<DP, MEASURE, FP8>(a, bh, packed & 0xffff, (float*)smem);
     return;
   }
   const int i = packed >> 16, t = packed & 0xffff;
