@@ -302,7 +302,7 @@ __device__ __forceinline__ void reuse_fold(const StepArgs& a, int bh, int row0, 
                                            int e_begin, int e_end, f32x16 (&acc)[DP / 32],
                                            float& m_row, float& l_row) {
   constexpr int NDT = DP / 32;
-  const int lane = threadIdx.x & 63, h32 = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, l32 = lane & 31;
   const int myrow = row0 + l32;
   const cint* ent = as_const(a.plan) + a.off_ent;
   const size_t slot_elems = (size_t)a.slot_rows * DP;
