@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import multiprocessing as mp
 import os
@@ -79,10 +80,15 @@ def mask_work(M, reuse_ptr, n, bh, D, cache_elem=2):
 
 
 def kernel_source_digest():
+    """Digest of the kernel sources' code: comments and whitespace are left out, so that a
+    comment edit keeps the stored counter figures valid."""
     h = hashlib.sha256()
     for f in ("dita_kernels.hip", "dita_internal.h"):
-        with open(os.path.join(ROOT, "partial_state_reuse_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "partial_state_reuse_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

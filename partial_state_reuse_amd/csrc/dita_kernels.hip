@@ -10,14 +10,22 @@
 // Kernels
 //   transpose_v     V [B,H,N,D] bf16 -> V^T scratch [B*H][DP][kt_pad] fp16, each partition's
 //                   key range padded with zeros to a multiple of the key tile.
-//   step_bf16<DP>   one workgroup (4 waves) per (b, h, query partition i, row tile).  For each
-//                   fresh j: flash-attention over j's keys with MFMA (S^T = K Q^T in bf16,
-//                   then O^T += V^T P^T in fp16), K and V^T tiles staged through LDS; at the block's end
-//                   the normalised state goes to the cache (bf16 O, f32 lse) and is folded
-//                   into the row's running merge.  For each reused j the cached state is
-//                   streamed with 16-byte loads and folded the same way.  The epilogue writes
-//                   out = acc / l (f32) and the row lse.
+//   step_bf16<DP, MEASURE, FP8, FIXED>
+//                   one workgroup (4 waves) per (b, h, query partition i, row tile), or per
+//                   tail sub-tile.  For each fresh j: flash-attention over j's keys with MFMA
+//                   (S^T = K Q^T in bf16, then O^T += V^T P^T in fp16), K and V^T tiles
+//                   staged through LDS; at the block's end the normalised state goes to the
+//                   cache (bf16 or fp8 O, f32 lse) and is folded into the row's running
+//                   merge.  For each reused j the cached state is streamed with 16-byte loads
+//                   and folded the same way.  The epilogue writes out = acc / l (f32) and the
+//                   row lse.  MEASURE adds the planner's measurement of the diagonal states'
+//                   change; FIXED is the fixed-reference pass (below), after which the FIXED =
+//                   false kernel runs as a conditional second pass.
 //   step_f32        the same computation in plain fp32 VALU arithmetic, one lane per row.
+//   snapshot_diag   the diagonal slots copied aside before a measuring bf16 step.
+//   planner_delta, planner_weights_part, planner_weights_sum
+//                   the planner's growth (per partition) and importance (per block) sums.
+//   merge_slots     group composition: cached states of a key group merged into one slot.
 //   read_slot       copies one cache slot out in plain row-major layout.
 //
 // Register layout of the bf16 kernel.  The 32x32x16 bf16 MFMA produces a 32x32 f32 tile in
@@ -158,13 +166,13 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 fused step.  Each wave owns a 32-row sub-tile of one query partition (lane l: query
-// row l%32).  Two kinds of workgroup, 4 waves each:
+// bf16 fused step.  Each wave works on a 32-row sub-tile of one query partition (lane l:
+// query row l%32).  Two kinds of workgroup, 4 waves each:
 //   group: the 4 waves take 128 consecutive rows of one partition and share every K / V^T
 //          tile, staged in LDS;
-//   tail:  4 independent sub-tiles (left over at the ends of partitions, possibly of
-//          different partitions); each wave reads its K / V^T fragments straight from
-//          global memory, with no LDS and no barrier.
+//   tail:  one sub-tile left over at the end of a partition; the 4 waves split its blocks,
+//          read their K / V^T fragments straight from global memory, and combine their
+//          partial merges through LDS at the end.
 // ------------------------------------------------------------------------------------------
 // Lazy rescale: the running reference m of a block state is raised only when a new logit
 // exceeds it by more than this many powers of two, so p = 2^(s - m) stays <= 2^8 and the
@@ -564,7 +572,7 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
 // MEASURE: the planner's measurement of the diagonal states' change is compiled in (a
 // separate instantiation, so that steps without it keep the leaner register allocation).
 // FP8: the cached O is fp8 e4m3 instead of bf16.
-// FIXED: the fixed-reference pass (row groups only; tail waves keep the running maximum).
+// FIXED: the fixed-reference pass (row groups only; tail workgroups keep the running maximum).
 template <int DP, bool MEASURE, bool FP8, bool FIXED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 3 : 1))) void step_bf16(StepArgs a) {
   constexpr int NKC = DP / 16;        // 16-wide d chunks of Q K^T
