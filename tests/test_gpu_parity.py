@@ -174,6 +174,39 @@ def test_ragged_bf16_geometries(dita, case):
     run_and_check(dita, cfg, heads=[(0, h) for h in range(H)])
 
 
+def _sweep_case(seed):
+    """A random small workload: geometry (1-4 frames, 3-16 x 3-24 grid, 1-10 partitions, so
+    partitions range from a few rows, handled by tail workgroups alone, to several row
+    groups), head dim, heads, steps, path (bf16 three times in four) and block policy."""
+    rng = np.random.default_rng(1000 + seed)
+    T, gh_, gw = int(rng.integers(1, 5)), int(rng.integers(3, 17)), int(rng.integers(3, 25))
+    N = T * gh_ * gw
+    P = int(rng.integers(1, min(10, N) + 1))
+    bf = bool(rng.random() < 0.75)
+    D = int(rng.choice([64, 72, 128] if bf else [16, 40, 64]))
+    H, S = int(rng.integers(1, 3)), int(rng.integers(2, 5))
+    kind = int(rng.integers(0, 4))
+    if kind == 0:
+        pol = Policy(kind=wcfg.FRESH_BUDGET, reuse_percent=int(rng.integers(0, 101)))
+    elif kind == 1:
+        pol = Policy(kind=wcfg.FRAME_THRESHOLD, max_fresh_frame_dist=int(rng.integers(0, 3)))
+    elif kind == 2:
+        pol = Policy(kind=wcfg.CENTROID_THRESHOLD, max_fresh_centroid2=int(rng.integers(0, 2 * N)))
+    else:
+        pol = Policy(kind=wcfg.FRAME_THRESHOLD, max_fresh_frame_dist=1, tile_sparse=True)
+    dt = "bf16" if bf else "f32"
+    return custom_config(name=f"sweep-{seed}", idx=200 + seed, heads=H, head_dim=D, frames=T,
+                         grid_h=gh_, grid_w=gw, num_partitions=P, steps=S, qkv_dtype=dt,
+                         cache_dtype=dt, schedule=wcfg.AnchorThen(pol))
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_geometry_sweep(dita, seed):
+    """Random small workloads, every element and every step against the oracle."""
+    cfg = _sweep_case(seed)
+    run_and_check(dita, cfg, heads=[(0, h) for h in range(cfg.heads)])
+
+
 def test_explicit_masks_and_custom_offsets_bf16(dita):
     """Explicit masks with skips and ragged hand-picked offsets (including a 1-token and a
     33-token partition)."""
