@@ -43,6 +43,20 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_fp8_cache_sweep(dita, seed):
+    """Random small workloads with the fp8 cache (2-6 frames, 3-12 x 3-20 grid, 2-10
+    partitions, head dim, schedule), sometimes with pairs or triples merged after the anchor."""
+    rng = np.random.default_rng(4000 + seed)
+    T, gh_, gw = int(rng.integers(2, 7)), int(rng.integers(3, 13)), int(rng.integers(3, 21))
+    P = int(rng.integers(2, 11))
+    D = int(rng.choice([64, 72, 128]))
+    H, S = int(rng.integers(1, 3)), int(rng.integers(2, 5))
+    kind = "budget" if rng.random() < 0.5 else "frame"
+    merges = {1: [(int(rng.integers(2, 4)), None)]} if rng.random() < 0.4 else None
+    test_fp8_cache(dita, (f"fp8-sweep-{seed}", T, gh_, gw, P, D, H, S, kind, merges))
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_fp8_cache(dita, case):
     import oracle

@@ -46,6 +46,28 @@ def _always_reused(masks, P, g):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_group_composition(dita, case):
+    run_group_case(dita, case)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_group_composition_sweep(dita, seed):
+    """Random small workloads (3-8 frames, 3-10 x 3-16 grid, 3-10 partitions, head dim, path)
+    with a random group size merged after the anchor (every eligible group, or the groups
+    every later step reuses whole) and sometimes again after step 2."""
+    rng = np.random.default_rng(3000 + seed)
+    T, gh_, gw = int(rng.integers(3, 9)), int(rng.integers(3, 11)), int(rng.integers(3, 17))
+    P = int(rng.integers(3, 11))
+    dt = "bf16" if rng.random() < 0.75 else "f32"
+    D = int(rng.choice([64, 72, 128] if dt == "bf16" else [16, 64]))
+    H, S = int(rng.integers(1, 3)), int(rng.integers(3, 6))
+    merges = {1: [(int(rng.integers(2, 5)), "sel" if rng.random() < 0.5 else None)]}
+    if rng.random() < 0.4:
+        merges[2] = [(int(rng.integers(2, P + 1)), None)]
+    run_group_case(dita, (f"groups-sweep-{seed}", T, gh_, gw, P, D, H, S, dt, merges),
+                   require_merge=False)
+
+
+def run_group_case(dita, case, require_merge=True):
     import oracle
     from oracle.policy import active_mask, partition_offsets
     name, T, gh_, gw, P, D, H, S, dt, merges = case
@@ -75,7 +97,8 @@ def test_group_composition(dita, case):
             n_merged.append(cache.merge_groups(g, select=sel))
     st = cache.stats()
     cache.free()
-    assert sum(n_merged) > 0
+    if require_merge:
+        assert sum(n_merged) > 0
     assert st["device_reuse_blocks"] == st["host_reuse_blocks"]
     log(f"groups merged: {n_merged}; states read on device {st['device_reuse_blocks']}")
 

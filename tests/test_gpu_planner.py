@@ -52,6 +52,26 @@ def test_planner_schedule(dita, case):
     run_planner_case(dita, case)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_planner_sweep(dita, seed):
+    """Random small workloads under the planner: geometry (2-6 frames, 3-12 x 3-20 grid, 3-10
+    partitions), head dim, path, reuse budget, group size, anchor period, error cap and the
+    tile-sparse set."""
+    rng = np.random.default_rng(5000 + seed)
+    T, gh_, gw = int(rng.integers(2, 7)), int(rng.integers(3, 13)), int(rng.integers(3, 21))
+    P = int(rng.integers(3, 11))
+    dt = str(rng.choice(["bf16", "bf16", "bf16/fp8", "f32"]))
+    D = int(rng.choice([64, 72, 128] if dt != "f32" else [16, 64]))
+    H, S = int(rng.integers(1, 3)), int(rng.integers(3, 7))
+    pct = int(rng.integers(30, 91))
+    G = int(rng.integers(1, 4))
+    period = int(rng.choice([0, 0, 3, 4]))
+    cap = float(rng.choice([0.0, 0.0, 5e-3]))
+    tile = bool(rng.random() < 0.25)
+    run_planner_case(dita, (f"planner-sweep-{seed}", T, gh_, gw, P, D, H, S, dt, pct, G, period,
+                            cap, tile), require_reuse=False)
+
+
 def test_planner_measures_through_a_second_pass(dita):
     """Steps after the anchor run the fixed-reference pass, which measures the growth against
     a snapshot of the old diagonal states (in its 128-row groups; tail waves keep the running
@@ -72,7 +92,7 @@ def test_planner_measures_through_a_second_pass(dita):
     run_planner_case(dita, case, modify=modify, recomputes="some")
 
 
-def run_planner_case(dita, case, modify=None, recomputes=None):
+def run_planner_case(dita, case, modify=None, recomputes=None, require_reuse=True):
     import oracle
     from oracle.policy import active_mask, partition_offsets, FRESH, SKIP
     name, T, gh_, gw, P, D, H, S, dt, pct, G, period, cap, tile = case
@@ -120,7 +140,8 @@ def run_planner_case(dita, case, modify=None, recomputes=None):
         want = oracle.planner_mask(offs, cfg.frame_tokens, pol, E, valid, False)
         assert np.array_equal(M, want), f"step {s}: planner decision differs"
         n_reuse_steps += int(np.any(M == 2))
-    assert n_reuse_steps > 0
+    if require_reuse:
+        assert n_reuse_steps > 0
     log(f"decisions: {S} steps equal, {n_reuse_steps} with reuse")
 
     # measurements against the oracle replaying the same masks (same cache rounding)
