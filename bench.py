@@ -108,6 +108,34 @@ def measured_traffic(digest, kernel, workload):
     return t.get("hbm_bytes_per_step")
 
 
+def describe_policy(pol, P):
+    """One-line description of a fixed block policy (for the bench line's config)."""
+    from workloads import configs as wc
+    if pol.anchor:
+        d = "anchor (every active block fresh)"
+    elif pol.kind == wc.FRAME_THRESHOLD:
+        d = f"fresh iff frame distance <= {pol.max_fresh_frame_dist}, else reused"
+    elif pol.kind == wc.CENTROID_THRESHOLD:
+        d = f"fresh iff doubled centroid distance <= {pol.max_fresh_centroid2}, else reused"
+    elif pol.kind == wc.FRESH_BUDGET:
+        r = min((pol.reuse_percent * P + 50) // 100, P - 1)
+        d = f"fresh budget {P - r}/{P} per row ({pol.reuse_percent} % reused)"
+    else:
+        d = f"policy kind {pol.kind}"
+    return d + ("; tile-sparse 3D frame mask" if pol.tile_sparse else "")
+
+
+def describe_schedule(cfg):
+    """The workload's fixed schedule as runs of steps with one policy each."""
+    parts, start = [], 1
+    for s in range(1, cfg.steps + 1):
+        if s == cfg.steps or cfg.policy(s + 1) != cfg.policy(s):
+            rng = f"step {start}" if start == s else f"steps {start}-{s}"
+            parts.append(f"{rng}: {describe_policy(cfg.policy(s), cfg.num_partitions)}")
+            start = s + 1
+    return "; ".join(parts)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,7 +215,7 @@ def main():
                          f"{args.planner_group}, anchor period {args.planner_anchor_period}")
     else:
         policies = [dita.policy_from(cfg.policy(s)) for s in range(1, S + 1)]
-        schedule_desc = "step 1 anchor (all fresh), then fresh budget 13/32 per row"
+        schedule_desc = describe_schedule(cfg)
     n_part = np.diff(dita.dita_partition_offsets(geom).astype(np.int64)).astype(np.float64)
     merge_sizes = [int(x) for x in args.merge.split(",") if x]
     merge_sel = []

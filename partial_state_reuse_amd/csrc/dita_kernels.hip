@@ -573,8 +573,11 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
 // separate instantiation, so that steps without it keep the leaner register allocation).
 // FP8: the cached O is fp8 e4m3 instead of bf16.
 // FIXED: the fixed-reference pass (row groups only; tail workgroups keep the running maximum).
+// Occupancy: 3 waves per SIMD at D <= 64 (168 VGPRs); 2 at D = 96 and 128, where the register
+// cap of 256 costs a few spills at block end only, and the second wave hides the latency
+// the single wave left exposed (the D = 128 step is about a quarter faster than at 1 wave).
 template <int DP, bool MEASURE, bool FP8, bool FIXED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 3 : 1))) void step_bf16(StepArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 3 : 2))) void step_bf16(StepArgs a) {
   constexpr int NKC = DP / 16;        // 16-wide d chunks of Q K^T
   constexpr int NDT = DP / 32;        // 32-row d tiles of O^T
   constexpr int KT = kKeyTile;        // keys per LDS tile
