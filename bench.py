@@ -108,6 +108,34 @@ def measured_traffic(digest, kernel, workload):
     return t.get("hbm_bytes_per_step")
 
 
+def hbm_roofline(traffic, cache_bytes_per_step, kernel_ms_per_step):
+    """The step kernels' HBM rate against the 8 TB/s peak: the counted traffic (rocprofv3
+    FETCH_SIZE + WRITE_SIZE per step) when the stored counters match this kernel and
+    workload, else the algorithmic cache bytes (reused states read + fresh states written
+    back), each over the step kernels' time per step."""
+    sec = kernel_ms_per_step * 1e-3
+    cache_gbs = cache_bytes_per_step / sec / 1e9
+    counted = traffic / sec / 1e9 if traffic else None
+    achieved = counted if counted is not None else cache_gbs
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "basis": "rocprofv3 FETCH_SIZE + WRITE_SIZE" if counted is not None
+            else "algorithmic cache bytes",
+            "cache_algorithmic_gb_s": round(cache_gbs, 1)}
+
+
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def describe_policy(pol, P):
     """One-line description of a fixed block policy (for the bench line's config)."""
     from workloads import configs as wc
@@ -330,6 +358,7 @@ def main():
                      "kernel_ms_per_step": round(avg_kernel_ms, 4),
                      "fresh_tflop_per_step": round(fresh_flops / launches / 1e12, 4),
                      "kernel_source_digest": digest},
+        "roofline_hbm": hbm_roofline(traffic, cache_bytes / K, avg_kernel_ms),
         "roofline_combined": {
             "t_roof_ms_per_step": round(t_roof_sum * 1e3 / K, 4),
             "frac_sum_form": round(t_roof_sum / wall, 4),
@@ -355,6 +384,7 @@ def main():
             "value": round(sample_flops / cpu_wall / 1e12, 6),
             "unit": "TFLOP/s",
             "cores": min(len(heads), args.workers),
+            "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"fp64 numpy oracle, heads {heads[0][1]}..{heads[-1][1]} of {H} "
                       f"(one process each, 1 BLAS thread), steps 1..{nsteps} of the same "
