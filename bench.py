@@ -124,6 +124,37 @@ def hbm_roofline(traffic, cache_bytes_per_step, kernel_ms_per_step):
             "cache_algorithmic_gb_s": round(cache_gbs, 1)}
 
 
+def time_offload(dita, cache, stream):
+    """One offload of the cache's state to pinned host memory and its restore into a new
+    device buffer, each timed with HIP events on the stream (host buffers allocated first)."""
+    import ctypes
+    import torch
+    n = cache.offload_bytes()
+    host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    new_buf = torch.empty(cache.required_bytes, dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    rc = dita._lib.dita_cache_offload(cache._h, ctypes.c_void_p(host.data_ptr()), n, sh)
+    ev[1].record(stream)
+    if rc:
+        raise dita.DitaError(rc, dita._lib.dita_last_error().decode())
+    ev[2].record(stream)
+    rc = dita._lib.dita_cache_restore(cache._h, ctypes.c_void_p(new_buf.data_ptr()),
+                                      cache.required_bytes, ctypes.c_void_p(host.data_ptr()),
+                                      n, sh)
+    ev[3].record(stream)
+    if rc:
+        raise dita.DitaError(rc, dita._lib.dita_last_error().decode())
+    torch.cuda.synchronize()
+    cache.buffer = new_buf
+    d2h, h2d = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    return {"bytes": n, "d2h_ms": round(d2h, 3), "h2d_ms": round(h2d, 3),
+            "d2h_gb_s": round(n / d2h / 1e6, 2), "h2d_gb_s": round(n / h2d / 1e6, 2),
+            "note": "host link, pinned memory; outside the timed steps"}
+
+
 def cpu_model():
     """The host CPU's model name (Linux /proc/cpuinfo), or None."""
     try:
@@ -181,6 +212,10 @@ def main():
                     help="comma-separated group sizes (e.g. 2,4): after each run's anchor step, "
                          "merge the cached states of every aligned key group that the schedule "
                          "reuses on all later steps, in that order (group composition)")
+    ap.add_argument("--offload", action="store_true",
+                    help="after the timed steps, time one offload of the cache's state to "
+                         "pinned host memory and its restore into a new device buffer "
+                         "(reported as `offload`, outside the timed region)")
     ap.add_argument("--planner-group", type=int, default=1)
     ap.add_argument("--planner-anchor-period", type=int, default=0)
     ap.add_argument("--cpu-heads", type=int, default=8)
@@ -371,6 +406,9 @@ def main():
             "device_fresh_blocks": st["device_fresh_blocks"],
             "host_fresh_blocks": st["host_fresh_blocks"]},
     }
+
+    if args.offload:
+        result["offload"] = time_offload(dita, cache, stream)
 
     if not args.no_cpu_baseline:
         heads = [(0, h) for h in range(min(args.cpu_heads, H))]

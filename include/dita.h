@@ -52,7 +52,9 @@ typedef enum dita_status {
   DITA_ERR_CACHE_MISS = 5,       /* REUSE of a slot not written since alloc / reset            */
   DITA_ERR_BUFFER_TOO_SMALL = 6, /* device buffer smaller than dita_cache_required_bytes       */
   DITA_ERR_NO_POLICY = 7,        /* dita_attn_step without a policy set for this step          */
-  DITA_ERR_DEVICE = 8            /* a HIP call failed (message in dita_last_error)             */
+  DITA_ERR_DEVICE = 8,           /* a HIP call failed (message in dita_last_error)             */
+  DITA_ERR_OFFLOADED = 9         /* the cache's state is offloaded to host memory
+                                    (dita_cache_offload); restore it first                    */
 } dita_status;
 
 /* DITA_FP8_E4M3: cache O only (with bf16 Q/K/V): OCP e4m3fn (1 sign, 4 exponent bits of bias
@@ -277,6 +279,40 @@ dita_status dita_set_profiling(dita_cache* cache, int32_t enable);
  * query `steps` first.  Errors: INVALID_ARGUMENT, DEVICE. */
 dita_status dita_get_planner_state(dita_cache* cache, float* w, double* delta,
                                    int32_t* fresh_step, int32_t* steps);
+
+/* Host offload of the state cache (DiTango, "Significato e Claim": the memory the state cache
+ * takes stays a constraint in production, and offloading it to the CPU is named as future
+ * work).
+ * For a caller that keeps several caches on one GPU, e.g. several generations in flight,
+ * and wants an idle cache's device memory back.  The offloaded state is the device counters
+ * followed by the cached lse and O of every slot; everything else in the buffer (work lists,
+ * V^T scratch, planner partials, merge jobs, snapshots) is rebuilt by the step that uses it.
+ *
+ * dita_cache_offload_bytes: host bytes the offloaded state takes (host only).
+ *
+ * dita_cache_offload: enqueue on hip_stream the copy of the state into host_dst (host, at
+ *   least dita_cache_offload_bytes; pinned memory from hipHostMalloc for the full link
+ *   rate) and mark the cache offloaded.  Stream-ordered: pass the stream of the last step or
+ *   merge on this cache (or synchronise first).  Once hip_stream has passed the copy, the
+ *   device buffer may be freed or reused.  host_dst must stay untouched until the restore.
+ *   While offloaded, dita_attn_step, dita_cache_merge_groups and dita_cache_read_slot fail
+ *   with OFFLOADED; policies may be set, plans read, the cache reset or freed, and
+ *   dita_get_stats reports the counters from host_dst.
+ *   Errors: INVALID_ARGUMENT (NULL pointer, too small, already offloaded), DEVICE.
+ *
+ * dita_cache_restore: bind device_buffer (device, 256-byte aligned, at least
+ *   dita_cache_required_bytes, on the device the cache ran on: the original buffer or
+ *   another) and enqueue on hip_stream the copy of the state back from host_src (host, as
+ *   written by dita_cache_offload; it must stay alive until hip_stream has passed the copy).
+ *   The cache then continues exactly where it stopped: slot validity, last-fresh steps,
+ *   merged groups and the planner's measurements are unchanged.
+ *   Errors: INVALID_ARGUMENT (not offloaded, NULL, misaligned, other device),
+ *   BUFFER_TOO_SMALL, DEVICE.  On error the cache stays offloaded. */
+dita_status dita_cache_offload_bytes(const dita_cache* cache, size_t* bytes);
+dita_status dita_cache_offload(dita_cache* cache, void* host_dst, size_t host_bytes,
+                               void* hip_stream);
+dita_status dita_cache_restore(dita_cache* cache, void* device_buffer, size_t buffer_bytes,
+                               const void* host_src, size_t host_bytes, void* hip_stream);
 
 /* Counters and last-step work.  Synchronises the device to read the device counters. */
 dita_status dita_get_stats(const dita_cache* cache, dita_step_stats* stats);

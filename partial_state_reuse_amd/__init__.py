@@ -25,7 +25,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 # ----- constants (include/dita.h) -----
 OK = 0
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "SHAPE", 3: "UNSUPPORTED", 4: "POLICY",
-                5: "CACHE_MISS", 6: "BUFFER_TOO_SMALL", 7: "NO_POLICY", 8: "DEVICE"}
+                5: "CACHE_MISS", 6: "BUFFER_TOO_SMALL", 7: "NO_POLICY", 8: "DEVICE",
+                9: "OFFLOADED"}
 F32, BF16, FP8_E4M3 = 0, 1, 2
 _DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 SKIP, FRESH, REUSE = 0, 1, 2
@@ -36,7 +37,8 @@ EXPORTED = ["dita_version", "dita_last_error", "dita_policy_mask", "dita_partiti
             "dita_cache_required_bytes", "dita_cache_alloc", "dita_cache_reset",
             "dita_cache_free", "dita_set_block_policy", "dita_get_block_plan",
             "dita_attn_step", "dita_cache_read_slot", "dita_set_profiling", "dita_get_stats",
-            "dita_planner_mask", "dita_get_planner_state", "dita_cache_merge_groups"]
+            "dita_planner_mask", "dita_get_planner_state", "dita_cache_merge_groups",
+            "dita_cache_offload_bytes", "dita_cache_offload", "dita_cache_restore"]
 
 
 class DitaError(RuntimeError):
@@ -104,6 +106,9 @@ _sig = {
                                          _f64p, _u8p, _u8p]),
     "dita_get_planner_state": (ctypes.c_int, [_P, _f32p, _f64p, _i32p, _i32p]),
     "dita_cache_merge_groups": (ctypes.c_int, [_P, ctypes.c_int32, _u8p, _i32p, _P]),
+    "dita_cache_offload_bytes": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
+    "dita_cache_offload": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    "dita_cache_restore": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -328,6 +333,43 @@ class Cache:
         _check(_lib.dita_cache_merge_groups(self._h, int(group), sptr, ctypes.byref(n),
                                             _P(_stream_handle(stream))))
         return n.value
+
+    def offload_bytes(self) -> int:
+        """Host bytes of the offloaded state (counters, cached lse and O of every slot)."""
+        n = ctypes.c_size_t(0)
+        _check(_lib.dita_cache_offload_bytes(self._h, ctypes.byref(n)))
+        return n.value
+
+    def offload(self, release=True, stream=None):
+        """Copy the cache's state into pinned host memory held by this object and mark the
+        cache offloaded.  With `release`, wait for the copy and drop the device buffer this
+        object holds (its memory goes back to torch's allocator)."""
+        import torch
+        host = torch.empty(self.offload_bytes(), dtype=torch.uint8, pin_memory=True)
+        _check(_lib.dita_cache_offload(self._h, _P(host.data_ptr()),
+                                       ctypes.c_size_t(host.numel()),
+                                       _P(_stream_handle(stream))))
+        self._host_state = host
+        if release:
+            torch.cuda.synchronize()
+            self.buffer = None
+
+    def restore(self, buffer=None, device=None, stream=None):
+        """Bind `buffer` (a uint8 device tensor of at least required_bytes; None: a new one)
+        and copy the offloaded state back; waits for the copy, then drops the host copy."""
+        import torch
+        host = getattr(self, "_host_state", None)
+        if host is None:
+            raise DitaError(1, "the cache is not offloaded by this object")
+        if buffer is None:
+            buffer = torch.empty(self.required_bytes, dtype=torch.uint8, device=device or "cuda")
+        _check(_lib.dita_cache_restore(self._h, _P(buffer.data_ptr()),
+                                       ctypes.c_size_t(buffer.numel() * buffer.element_size()),
+                                       _P(host.data_ptr()), ctypes.c_size_t(host.numel()),
+                                       _P(_stream_handle(stream))))
+        self.buffer = buffer
+        torch.cuda.synchronize()
+        self._host_state = None
 
     def planner_state(self) -> dict:
         """The planner's measured state (waits for the last step's measurements)."""

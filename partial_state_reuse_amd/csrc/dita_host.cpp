@@ -364,6 +364,15 @@ struct Layout {
          wpart = 0, merge = 0, merge_bytes = 0, snap = 0, total = 0;
 };
 
+// The persistent part of the device buffer, as offloaded to the host: the counters, then
+// the cached lse and O of every slot (the [lse, delta) span of the layout).  The rest (work
+// lists, V^T, planner partials, merge jobs, snapshots) is rebuilt by the step that uses it.
+size_t offload_counter_bytes(const Layout& L) { return L.plans - L.counters; }
+size_t offload_state_bytes(const Layout& L) { return L.delta - L.lse; }
+size_t offload_total_bytes(const Layout& L) {
+  return offload_counter_bytes(L) + offload_state_bytes(L);
+}
+
 Layout compute_layout(const Geo& g, int num_slots) {
   Layout L;
   const size_t P = g.P;
@@ -444,6 +453,9 @@ struct dita_cache {
   std::vector<int32_t> last_fresh;   // P*P step at which the slot was written (0 = never)
   bool has_pending = false;
   Plan pending;
+  // host offload: the persistent device state lives in offload_host until the restore
+  bool offloaded = false;
+  const void* offload_host = nullptr;
   bool has_last = false;
   Plan last;
   int64_t steps_done = 0;
@@ -898,6 +910,7 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
       return fail(DITA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
   if (lse_out && (uintptr_t)lse_out % 4 != 0)
     return fail(DITA_ERR_INVALID_ARGUMENT, "lse_out must be 4-byte aligned");
+  if (c->offloaded) return fail(DITA_ERR_OFFLOADED, "the cache is offloaded; restore it first");
   if (!c->has_pending) return fail(DITA_ERR_NO_POLICY, "no block policy set for this step");
   hipStream_t s = (hipStream_t)hip_stream;
   dita_status st = device_init(c, s);
@@ -1026,6 +1039,7 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
 dita_status dita_cache_read_slot(dita_cache* c, int32_t b, int32_t h, int32_t i, int32_t j,
                                  float* o_out, float* lse_out, void* hip_stream) {
   if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (c->offloaded) return fail(DITA_ERR_OFFLOADED, "the cache is offloaded; restore it first");
   const Geo& g = c->g;
   if (b < 0 || b >= g.B || h < 0 || h >= g.H || i < 0 || i >= g.P || j < 0 || j >= g.P)
     return fail(DITA_ERR_INVALID_ARGUMENT, "slot index out of range");
@@ -1058,6 +1072,7 @@ dita_status dita_cache_merge_groups(dita_cache* c, int32_t group, const uint8_t*
                                     int32_t* merged, void* hip_stream) {
   if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
   if (group < 2) return fail(DITA_ERR_INVALID_ARGUMENT, "group must be >= 2");
+  if (c->offloaded) return fail(DITA_ERR_OFFLOADED, "the cache is offloaded; restore it first");
   if (c->has_pending)
     return fail(DITA_ERR_INVALID_ARGUMENT, "merge between steps, before the next policy is set");
   if ((int64_t)c->g.B * c->g.H > 65535 || c->g.slot_rows / 32 > 65535)
@@ -1168,6 +1183,78 @@ dita_status dita_get_planner_state(dita_cache* c, float* w, double* delta, int32
   return ok();
 }
 
+dita_status dita_cache_offload_bytes(const dita_cache* c, size_t* bytes) {
+  if (!c || !bytes) return fail(DITA_ERR_INVALID_ARGUMENT, "cache and bytes required");
+  *bytes = offload_total_bytes(c->L);
+  return ok();
+}
+
+dita_status dita_cache_offload(dita_cache* c, void* host_dst, size_t host_bytes,
+                               void* hip_stream) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (c->offloaded) return fail(DITA_ERR_INVALID_ARGUMENT, "the cache is already offloaded");
+  if (!host_dst) return fail(DITA_ERR_INVALID_ARGUMENT, "host_dst is NULL");
+  const size_t need = offload_total_bytes(c->L);
+  if (host_bytes < need)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "host_dst holds %zu bytes, %zu needed", host_bytes,
+                need);
+  hipStream_t s = (hipStream_t)hip_stream;
+  uint8_t* h = (uint8_t*)host_dst;
+  dita_status st = hip_check(hipMemcpyAsync(h, c->dev + c->L.counters,
+                                            offload_counter_bytes(c->L),
+                                            hipMemcpyDeviceToHost, s), "offload copy");
+  if (st) return st;
+  st = hip_check(hipMemcpyAsync(h + offload_counter_bytes(c->L), c->dev + c->L.lse,
+                                offload_state_bytes(c->L), hipMemcpyDeviceToHost, s),
+                 "offload copy");
+  if (st) return st;
+  c->offloaded = true;
+  c->offload_host = host_dst;
+  return ok();
+}
+
+dita_status dita_cache_restore(dita_cache* c, void* device_buffer, size_t buffer_bytes,
+                               const void* host_src, size_t host_bytes, void* hip_stream) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!c->offloaded) return fail(DITA_ERR_INVALID_ARGUMENT, "the cache is not offloaded");
+  if (!device_buffer || !host_src)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "device_buffer and host_src required");
+  if ((uintptr_t)device_buffer % 256 != 0)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "device_buffer must be 256-byte aligned");
+  if (buffer_bytes < c->L.total)
+    return fail(DITA_ERR_BUFFER_TOO_SMALL, "buffer holds %zu bytes, %zu needed", buffer_bytes,
+                c->L.total);
+  const size_t need = offload_total_bytes(c->L);
+  if (host_bytes < need)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "host_src holds %zu bytes, %zu needed", host_bytes,
+                need);
+  if (c->dev_init) {
+    int dev = -1;
+    dita_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (st) return st;
+    if (dev != c->device)
+      return fail(DITA_ERR_INVALID_ARGUMENT, "restore on device %d, the cache ran on device %d",
+                  dev, c->device);
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  uint8_t* d = (uint8_t*)device_buffer;
+  const uint8_t* h = (const uint8_t*)host_src;
+  dita_status st = hip_check(hipMemcpyAsync(d + c->L.counters, h, offload_counter_bytes(c->L),
+                                            hipMemcpyHostToDevice, s), "restore copy");
+  if (st) return st;
+  st = hip_check(hipMemcpyAsync(d + c->L.lse, h + offload_counter_bytes(c->L),
+                                offload_state_bytes(c->L), hipMemcpyHostToDevice, s),
+                 "restore copy");
+  if (st) return st;
+  c->dev = d;
+  c->dev_bytes = buffer_bytes;
+  // the uploaded work lists lived in the old buffer
+  for (auto& ps : c->pslots) ps.used = false;
+  c->offloaded = false;
+  c->offload_host = nullptr;
+  return ok();
+}
+
 dita_status dita_get_stats(const dita_cache* cc, dita_step_stats* s) {
   if (!cc || !s) return fail(DITA_ERR_INVALID_ARGUMENT, "cache and stats required");
   dita_cache* c = const_cast<dita_cache*>(cc);   // draining timing events updates sums only
@@ -1189,9 +1276,13 @@ dita_status dita_get_stats(const dita_cache* cc, dita_step_stats* s) {
     unsigned long long cnt[4] = {0, 0, 0, 0};
     dita_status st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
     if (st) return st;
-    st = hip_check(hipMemcpy(cnt, c->dev + c->L.counters, sizeof cnt, hipMemcpyDeviceToHost),
-                   "counter read");
-    if (st) return st;
+    if (c->offloaded) {
+      std::memcpy(cnt, c->offload_host, sizeof cnt);   // the offload copy has completed
+    } else {
+      st = hip_check(hipMemcpy(cnt, c->dev + c->L.counters, sizeof cnt, hipMemcpyDeviceToHost),
+                     "counter read");
+      if (st) return st;
+    }
     s->device_fresh_blocks = cnt[0];
     s->device_reuse_blocks = cnt[1];
     s->device_v_range_errors = cnt[2];

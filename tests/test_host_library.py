@@ -219,3 +219,35 @@ def test_geometry_errors():
     with pytest.raises(dita.DitaError) as e:
         dita.Cache(g, buffer_ptr=FAKE + 16, buffer_bytes=1 << 30)
     assert e.value.name == "INVALID_ARGUMENT"
+
+
+@pytest.mark.parametrize("idx,cache", [(2, "bf16"), (3, "bf16"), (3, "fp8"), (1, "f32")])
+def test_offload_size_and_argument_errors(idx, cache):
+    """Host offload (no device work): the offloaded state holds at least every slot's cached
+    O and lse (n_i rows of D elements of the cache precision plus one f32 each, per (b, h) and
+    active block) and at most the whole device buffer; calls that cannot proceed fail before
+    any copy is enqueued."""
+    import ctypes
+    import dataclasses
+    cfg = dataclasses.replace(CONFIGS[idx], cache_dtype=cache)
+    offs = partition_offsets(cfg.tokens, cfg.num_partitions)
+    act = active_mask(offs, cfg.frame_tokens, cfg.policy(1).tile_sparse)
+    c, g = fake_cache(cfg, act.astype(np.uint8))
+    n = c.offload_bytes()
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[cache]
+    rows = np.diff(np.asarray(offs, np.int64))
+    state = int(sum(rows[i] * (cfg.head_dim * esz + 4)
+                    for i in range(cfg.num_partitions) for j in range(cfg.num_partitions)
+                    if act[i, j])) * cfg.batch * cfg.heads
+    assert state < n <= c.required_bytes
+    lib = dita._lib
+    small = (ctypes.c_uint8 * 64)()
+    assert lib.dita_cache_offload(c._h, None, n, None) == 1                  # host_dst NULL
+    assert lib.dita_cache_offload(c._h, ctypes.cast(small, ctypes.c_void_p), 64, None) == 1
+    assert lib.dita_cache_restore(c._h, dita._P(FAKE), c.required_bytes,
+                                  ctypes.cast(small, ctypes.c_void_p), n, None) == 1
+    assert "not offloaded" in dita._lib.dita_last_error().decode()
+    size = ctypes.c_size_t(0)
+    assert lib.dita_cache_offload_bytes(None, ctypes.byref(size)) == 1
+    assert lib.dita_cache_offload_bytes(c._h, None) == 1
+    c.free()
