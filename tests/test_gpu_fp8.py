@@ -5,8 +5,12 @@ states to e4m3 the same way (nearest even, saturating).  The GPU and the oracle 
 that differ by their arithmetic error, so a cached element can land one e4m3 spacing apart on
 the two sides; each reused state r enters the output with weight w_r = exp(lse_r - L), so the
 element-wise bar is the bf16 output bar plus sum over reused states of w_r * spacing(|O_r|).
-lse does not depend on the O rounding and keeps the bf16 bar.  The distance to the exact
-(fp64, unrounded) result is logged: it is the accuracy the compression costs."""
+A state merged from a group (group composition) is rounded twice: its members' cached states
+(each possibly one spacing apart) enter the merge with their shares exp(lse_m - L_group), and
+the merged result is rounded again, so its term is w_r * (spacing(|O_r|) + sum over members of
+share_m * spacing(|O_m|)).  lse does not depend on the O rounding and keeps the bf16 bar.  The
+distance to the exact (fp64, unrounded) result is logged: it is the accuracy the compression
+costs."""
 import numpy as np
 import pytest
 
@@ -32,6 +36,19 @@ def spacing8(x):
     ax = np.abs(np.asarray(x, np.float64))
     k = np.floor(np.log2(np.where(ax > 0, ax, 2.0 ** -9)))
     return np.exp2(np.maximum(k, -6.0) - 3.0)
+
+
+def merged_members(r, i, j, merges, P):
+    """The blocks whose states the state read at (i, j) merges (j included), or [] if it is
+    not a merged state.  Merges here are one level, after step 1: members of a merged group
+    show REUSE in the mask without a state of their own."""
+    if not merges:
+        return []
+    assert list(merges) == [1] and len(merges[1]) == 1, "one merge level, after step 1"
+    g = merges[1][0][0]
+    covered = [m for m in range(P) if m != j and m // g == j // g and r.mask[i, m] == 2
+               and (i, m) not in r.block_o]
+    return [j] + covered if covered else []
 
 
 CASES = [
@@ -111,7 +128,12 @@ def test_fp8_cache(dita, case):
                 for j in range(P):
                     if r.mask[i, j] == 2 and (i, j) in r.block_o:
                         wgt = np.exp(r.block_lse[(i, j)] - r.lse[rows])
-                        bound[rows] += wgt[:, None] * spacing8(r.block_o[(i, j)])
+                        sp = spacing8(r.block_o[(i, j)])
+                        for m in merged_members(r, i, j, merges, P):
+                            # members hold their anchor-step states (merged after step 1)
+                            share = np.exp(emu[0].block_lse[(i, m)] - r.block_lse[(i, j)])
+                            sp = sp + share[:, None] * spacing8(emu[0].block_o[(i, m)])
+                        bound[rows] += wgt[:, None] * sp
             err = np.abs(outs[s][b, h] - r.out)
             slack = float((err - bound).max())
             lerr = float(np.abs(lses[s][b, h] - r.lse).max())

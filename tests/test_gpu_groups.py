@@ -2,12 +2,19 @@
 Dinamica dei Gruppi"), through the C ABI: cached states merged into coarser groups after a
 step, then reused as one state.  Masks (with whole-group promotion) and reuse lists are
 compared bit for bit with the oracle; outputs of every step against the fp64 oracle on the
-same merges within the bf16 / f32 bars; device-counted reads against the host plan."""
+same merges within the bf16 / f32 bars; device-counted reads against the host plan.
+
+A merged state is rounded to the cache precision once more per merge level than a state
+reused as it was written, by at most half a unit in the last place of its magnitude; every
+state is a convex combination of V rows, so that magnitude is at most max |V| over the
+group's keys.  The output bar therefore grows, per merged state r read with weight
+w_r = exp(lse_r - L), by w_r * levels * ulp(max |V|) / 2.  Without merges it is the plain
+bar."""
 import numpy as np
 import pytest
 
 import gpu_helpers as gh
-from gpu_helpers import compare, log
+from gpu_helpers import BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, log
 from workloads import Policy, custom_config
 from workloads import configs as wcfg
 
@@ -67,6 +74,36 @@ def test_group_composition_sweep(dita, seed):
                    require_merge=False)
 
 
+def ulp(x, bf16):
+    """Unit in the last place of bf16 (8 significant bits) or f32 (24) at |x|."""
+    ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - (7 if bf16 else 23))
+
+
+def merge_rounding_bar(r, offs, P, resolved, inputs, step, bf16):
+    """Extra output allowance [N, D] at 0-based step `step` for the merged states read there:
+    w_r * levels * ulp(max |V| over the group's keys and the steps so far) / 2."""
+    levels = [g for t, lst in resolved.items() if t <= step for (g, _) in lst]
+    extra = np.zeros((offs[-1], inputs[0][2].shape[1]))
+    if not levels:
+        return extra
+    G = max(levels)
+    vmax = [max(float(np.abs(inputs[t][2][offs[j]:offs[j + 1]]).max()) for t in range(step + 1))
+            for j in range(P)]
+    for i in range(P):
+        rows = slice(offs[i], offs[i + 1])
+        for j in range(P):
+            if r.mask[i, j] != 2 or (i, j) not in r.block_o:
+                continue
+            group = [m for m in range(P) if m // G == j // G]
+            if not any(m != j and r.mask[i, m] == 2 and (i, m) not in r.block_o for m in group):
+                continue                                   # not a merged state
+            w = np.exp(r.block_lse[(i, j)] - r.lse[rows])
+            vm = max(vmax[m] for m in group)
+            extra[rows] += (w * len(levels) * 0.5 * float(ulp(vm, bf16)))[:, None]
+    return extra
+
+
 def run_group_case(dita, case, require_merge=True):
     import oracle
     from oracle.policy import active_mask, partition_offsets
@@ -103,16 +140,22 @@ def run_group_case(dita, case, require_merge=True):
     log(f"groups merged: {n_merged}; states read on device {st['device_reuse_blocks']}")
 
     ok = True
+    bf = dt == "bf16"
     for (b, h) in heads:
         ref = oracle.run_head(cfg, b, h, cache_mode="fp64", merges=resolved, active=act,
-                              inputs=kept[(b, h)])
+                              inputs=kept[(b, h)], keep_block_lse=True)
         for s in range(S):
             p, r = plans[s], ref[s]
             assert np.array_equal(p["mask"], r.mask), f"step {s + 1}: mask"
             assert np.array_equal(p["reuse_ptr"], r.reuse_ptr), f"step {s + 1}: reuse_ptr"
             assert np.array_equal(p["reuse_cols"], r.reuse_cols), f"step {s + 1}: reuse_cols"
-            o, *_ = compare(outs[s][b, h], r.out, dt == "bf16", f"step {s + 1} head {h} out")
-            ok &= o
+            err = np.abs(np.asarray(outs[s][b, h], np.float64) - r.out)
+            extra = merge_rounding_bar(r, offs, P, resolved, kept[(b, h)], s, bf)
+            bar = (BF16_MAX_ABS if bf else F32_MAX_ABS) + extra
+            good = bool(np.all(err <= bar)) and (not bf or float(err.mean()) <= BF16_MEAN_ABS)
+            log(f"step {s + 1} head {h} out: max-abs {err.max():.3e} mean-abs {err.mean():.3e} "
+                f"(largest merge allowance {extra.max():.2e}) {'ok' if good else 'FAIL'}")
+            ok &= good
             lerr = float(np.abs(lses[s][b, h] - r.lse).max())
             ok &= lerr < (2e-3 if dt == "bf16" else 1e-5)
     assert ok

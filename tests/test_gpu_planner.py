@@ -24,7 +24,18 @@ torch = pytest.importorskip("torch")
 # importance: lse in f32 on both sides; growth: RMS of differences of bf16-rounded states,
 # where a value near a rounding boundary can land one ulp apart on the two sides
 W_RTOL, W_ATOL = 2e-4, 1e-7
-DELTA_RTOL = {"bf16": 5e-3, "f32": 1e-4, "fp8": 1e-2}
+DELTA_RTOL = {"bf16": 5e-3, "f32": 1e-4}
+
+
+def fp8_delta_rtol(n):
+    """Relative bar on the growth with an fp8 (e4m3) cache, over an RMS of n elements.  Both
+    sides round the new and the old diagonal state to e4m3, whose spacing (1/16 to 1/8 of the
+    value) is about the size of one step's change, from values that differ by their
+    arithmetic error: the elements near a rounding midpoint (about a tenth) may land one
+    spacing apart, in random places and directions.  Their effect on the RMS shrinks like
+    1/sqrt(n), about 0.3/sqrt(n) for one standard deviation; the bar is 1/sqrt(n), and never
+    under 1e-2."""
+    return max(1e-2, 1.0 / np.sqrt(n))
 
 
 @pytest.fixture(scope="module")
@@ -156,7 +167,13 @@ def run_planner_case(dita, case, modify=None, recomputes=None, require_reuse=Tru
             got = st["delta"][s - 1]
             rel = np.abs(got - ref.delta) / np.maximum(ref.delta, 1e-12)
             log(f"step {s}: growth {np.round(got, 5).tolist()} rel err max {rel.max():.2e}")
-            assert np.all(rel <= DELTA_RTOL[cdt]), f"step {s}: growth rel err {rel.max():.3e}"
+            if cdt == "fp8":
+                rows = np.diff(np.asarray(offs, np.int64))
+                bar = np.array([fp8_delta_rtol(len(heads) * int(rows[i]) * cfg.head_dim)
+                                for i in range(P)])
+            else:
+                bar = DELTA_RTOL[cdt]
+            assert np.all(rel <= bar), f"step {s}: growth rel err {rel.max():.3e}"
 
     if cdt != dt:
         return
