@@ -969,7 +969,16 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
       st = hip_check(hipEventRecord(ts->ev[1], s), "hipEventRecord");
       if (st) return st;
     }
-    st = hip_check(dita::launch_step_bf16(a, s), "bf16 step launch");
+    if (snap) {
+      // the step runs the plain kernels; the diagonal states' change against the snapshot is
+      // measured after both of its passes
+      dita::StepArgs plain = a;
+      plain.delta_part = nullptr;
+      st = hip_check(dita::launch_step_bf16(plain, s), "bf16 step launch");
+      if (!st) st = hip_check(dita::launch_diag_change(a, s), "diag_change launch");
+    } else {
+      st = hip_check(dita::launch_step_bf16(a, s), "bf16 step launch");
+    }
   } else {
     if (ts) {
       st = hip_check(hipEventRecord(ts->ev[1], s), "hipEventRecord");

@@ -100,6 +100,8 @@ hipError_t launch_step_f32(const StepArgs& a, hipStream_t s);
 inline int planner_chunks(int P) { return P >= 2048 ? 1 : (2048 / P > 64 ? 64 : 2048 / P); }
 hipError_t launch_planner_delta(const StepArgs& a, float* delta, hipStream_t s);
 hipError_t launch_snapshot_diag(const StepArgs& a, hipStream_t s);
+// the diagonal states' change against the snapshot, after a measuring step (bf16 path)
+hipError_t launch_diag_change(const StepArgs& a, hipStream_t s);
 hipError_t launch_planner_weights(const StepArgs& a, float* w, float* part, hipStream_t s);
 // Group composition: job k = jobs[4k..4k+3] = {n_i, dst slot, first source, sources}; the
 // sources are slot numbers in srcs.  Grid (njobs, slot_rows / 32 sub-tiles, B*H).

@@ -23,6 +23,7 @@
 //                   false kernel runs as a conditional second pass.
 //   step_f32        the same computation in plain fp32 VALU arithmetic, one lane per row.
 //   snapshot_diag   the diagonal slots copied aside before a measuring bf16 step.
+//   diag_change     after it, the diagonal states' squared change against that copy.
 //   planner_delta, planner_weights_part, planner_weights_sum
 //                   the planner's growth (per partition) and importance (per block) sums.
 //   merge_slots     group composition: cached states of a key group merged into one slot.
@@ -570,7 +571,9 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
 }
 
 // MEASURE: the planner's measurement of the diagonal states' change is compiled in (a
-// separate instantiation, so that steps without it keep the leaner register allocation).
+// separate instantiation, so that steps without it keep the leaner register allocation); used
+// only where no snapshot of the old diagonal states is taken, since with one the step runs
+// the plain kernel and diag_change measures afterwards.
 // FP8: the cached O is fp8 e4m3 instead of bf16.
 // FIXED: the fixed-reference pass (row groups only; tail workgroups keep the running maximum).
 // Occupancy: 3 waves per SIMD at D <= 64 (168 VGPRs); 2 at D = 96 and 128, where the register
@@ -956,6 +959,65 @@ __global__ __launch_bounds__(256) void snapshot_diag(StepArgs a, int slot_bytes)
   for (int w = threadIdx.x; w < slot_bytes / 16; w += 256) dst[w] = src[w];
 }
 
+// The change of the diagonal states a measuring step wrote, against the snapshot of them taken
+// before the step: per (b, h, i, 32-row sub-tile) the sum over rows < n_i and d < D of
+// (new - old)^2, summed in block_end's order (per lane over d tiles and accumulator rows, then
+// over the wave), into delta_part.  Grid (P, B*H); one wave per sub-tile.
+template <int DP, bool FP8>
+__global__ __launch_bounds__(256) void diag_change(StepArgs a) {
+  constexpr int NDT = DP / 32;
+  typedef typename CacheElem<FP8>::type CT;
+  const int i = blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h32 = lane >> 5, l32 = lane & 31;
+  const cint* plan = as_const(a.plan);
+  const cint* offs = plan + a.off_offs;
+  const cint* rinfo = plan + a.off_rows + 4 * i;
+  const cint* ent = plan + a.off_ent;
+  const int n_i = offs[i + 1] - offs[i];
+  const int e0 = rinfo[0], nf = rinfo[1];
+  int slot = -1;
+  for (int e = 0; e < nf; ++e)
+    if (ent[2 * (e0 + e)] == i) slot = ent[2 * (e0 + e) + 1];
+  if (slot < 0) return;
+  const size_t slot_elems = (size_t)a.slot_rows * DP;
+  const CT* nw = (const CT*)a.cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems;
+  const CT* od = (const CT*)a.diag_snap + ((size_t)bh * a.P + i) * slot_elems;
+  const int S = (n_i + 31) / 32;
+  for (int t = wave; t < S; t += kWaves) {               // wave-uniform
+    const int myrow = t * 32 + l32;
+    const CT* nt = nw + (size_t)t * 32 * DP;
+    const CT* ot = od + (size_t)t * 32 * DP;
+    float sq = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      float nv[16], ov[16];
+      if constexpr (FP8) {
+        fp8_unpack16(ld16(nt + dt * 1024 + lane * 16), nv);
+        fp8_unpack16(ld16(ot + dt * 1024 + lane * 16), ov);
+      } else {
+        const bf16x8 n0 = as_bf16x8(ld16(nt + dt * 1024 + lane * 16));
+        const bf16x8 n1 = as_bf16x8(ld16(nt + dt * 1024 + lane * 16 + 8));
+        const bf16x8 p0 = as_bf16x8(ld16(ot + dt * 1024 + lane * 16));
+        const bf16x8 p1 = as_bf16x8(ld16(ot + dt * 1024 + lane * 16 + 8));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          nv[r] = (float)n0[r]; nv[r + 8] = (float)n1[r];
+          ov[r] = (float)p0[r]; ov[r + 8] = (float)p1[r];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // accumulator row r of d tile dt holds d = dt*32 + 8*(r/4) + 4*h32 + r%4
+        const int d = dt * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        const float df = nv[r] - ov[r];
+        if (myrow < n_i && d < a.D) sq = __builtin_fmaf(df, df, sq);
+      }
+    }
+    sq = wave_sum(sq);
+    if (lane == 0) a.delta_part[((size_t)bh * a.P + i) * a.delta_stride + t] = sq;
+  }
+}
+
 __device__ __forceinline__ void block_sum(double* red, double x) {
   red[threadIdx.x] = x;
   __syncthreads();
@@ -1192,6 +1254,21 @@ hipError_t launch_step_f32(const StepArgs& a, hipStream_t s) {
 hipError_t launch_snapshot_diag(const StepArgs& a, hipStream_t s) {
   const int slot_bytes = a.slot_rows * a.DP * (a.cache_fp8 ? 1 : 2);
   hipLaunchKernelGGL(snapshot_diag, dim3(a.P, a.B * a.H), dim3(256), 0, s, a, slot_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_diag_change(const StepArgs& a, hipStream_t s) {
+  const dim3 grid(a.P, a.B * a.H);
+#define DITA_LAUNCH_DC(DPV)                                                                      \
+  if (a.cache_fp8) hipLaunchKernelGGL((diag_change<DPV, true>), grid, dim3(256), 0, s, a);       \
+  else hipLaunchKernelGGL((diag_change<DPV, false>), grid, dim3(256), 0, s, a);
+  switch (a.DP) {
+    case 64: DITA_LAUNCH_DC(64) break;
+    case 96: DITA_LAUNCH_DC(96) break;
+    case 128: DITA_LAUNCH_DC(128) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DITA_LAUNCH_DC
   return hipGetLastError();
 }
 
