@@ -215,7 +215,18 @@ def test_geometry_errors():
     assert err(offsets=[0, 10, 10, 40, 64]) == "SHAPE"
     assert err(offsets=[0, 10, 20, 40, 63]) == "SHAPE"
     assert err(batch=0) == "SHAPE"
+    # limits: at most 1024 partitions, partitions under 2^21 rows, tensors under 2^40 elements
+    assert err(tokens=2048, frames=8, grid_h=16, grid_w=16, num_partitions=1025) == "SHAPE"
+    assert err(tokens=1 << 21, frames=32, grid_h=256, grid_w=256, num_partitions=1) == "SHAPE"
+    assert err(batch=1 << 10, heads=1 << 10, tokens=1 << 14, frames=1, grid_h=128, grid_w=128,
+               head_dim=64) == "SHAPE"
+    assert err(dtype="f32", cache_dtype="fp8") == "UNSUPPORTED"
+    big = dita.make_geometry(1, 1, 1024, 64, 4, 16, 16, 1024, "bf16")   # P = N = 1024: accepted
+    assert dita.dita_cache_required_bytes(big) > 0
     g = dita.make_geometry(1, 1, 64, 64, 4, 4, 4, 4, "bf16")
+    with pytest.raises(dita.DitaError) as e:
+        dita.Cache(g, buffer_ptr=FAKE, buffer_bytes=dita.dita_cache_required_bytes(g) - 256)
+    assert e.value.name == "BUFFER_TOO_SMALL"
     with pytest.raises(dita.DitaError) as e:
         dita.Cache(g, buffer_ptr=FAKE + 16, buffer_bytes=1 << 30)
     assert e.value.name == "INVALID_ARGUMENT"
