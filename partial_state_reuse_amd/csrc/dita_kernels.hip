@@ -19,8 +19,9 @@
 //                   merge.  For each reused j the cached state is streamed with 16-byte loads
 //                   and folded the same way.  The epilogue writes out = acc / l (f32) and the
 //                   row lse.  MEASURE adds the planner's measurement of the diagonal states'
-//                   change; FIXED is the fixed-reference pass (below), after which the FIXED =
-//                   false kernel runs as a conditional second pass.
+//                   change, for steps that take no snapshot of them (otherwise diag_change
+//                   measures after the step); FIXED is the fixed-reference pass (below),
+//                   after which the FIXED = false kernel runs as a conditional second pass.
 //   step_f32        the same computation in plain fp32 VALU arithmetic, one lane per row.
 //   snapshot_diag   the diagonal slots copied aside before a measuring bf16 step.
 //   diag_change     after it, the diagonal states' squared change against that copy.
