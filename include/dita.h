@@ -152,11 +152,12 @@ typedef struct dita_step_stats {
   double prep_kernel_ms;         /* summed duration of the V-transpose kernel (bf16 only)    */
   uint64_t device_ref_recomputes;/* cumulative: bf16 steps computed a second time.  When every
                                     fresh block of a step has a state from an earlier step,
-                                    the step first runs with each row's cached lse as its fixed
-                                    softmax reference (no running maximum); if a row's sum then
-                                    falls outside [2^2, 2^15] (a block's lse moved by more than
-                                    about 6 powers of two since it was cached) the whole step
-                                    is computed again with the running maximum.  Results are
+                                    the step first runs with each block's cached lse (per row)
+                                    as its fixed softmax reference (no running maximum); if a
+                                    row's sum over a block then falls outside [2^2, 2^15] (the
+                                    block's lse moved by more than about 6 powers of two since
+                                    it was cached) the whole step is computed again with the
+                                    running maximum.  Results are
                                     the same either way, within rounding.                     */
 } dita_step_stats;
 
