@@ -8,8 +8,8 @@ The policies are plain parameter records (kind + thresholds); how a policy turns
 fresh/reuse/skip mask is defined twice, independently: once in the fp64 oracle and once in
 the native host library.  Nothing in this module computes attention or a mask.
 
-Sources for the shapes and schedules (the pages give no numbers for them; the readings are
-listed in DESIGN.md):
+Sources for the shapes and schedules (the pages give no numbers for them; the shapes below
+are readings consistent with them):
   * DiTango (gist.science 2607.15650), "Metodologia / Anchor-Guided Selection Planner":
     partitions are computed fresh or reuse an earlier step's attention state; anchor steps
     recompute everything; the local partition is always computed.

@@ -1,6 +1,6 @@
 """Seeded synthetic Q/K/V generator shared by the oracle's tests, the GPU tests and the bench.
 
-It holds no attention arithmetic: it only draws inputs.  The recipe (stated in the design doc):
+It holds no attention arithmetic: it only draws inputs.  The recipe:
 
   * token position (t, y, x), flattened frame-major then row-major;
   * a sinusoidal position term PE in R^D.  3D: channel blocks [t | y | x] of widths
