@@ -212,6 +212,9 @@ def main():
                     help="comma-separated group sizes (e.g. 2,4): after each run's anchor step, "
                          "merge the cached states of every aligned key group that the schedule "
                          "reuses on all later steps, in that order (group composition)")
+    ap.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
+                    help="layout of Q, K, V and out: [B, H, N, D] or [B, N, H, D] (the inputs "
+                         "are staged in that layout before the timed region)")
     ap.add_argument("--offload", action="store_true",
                     help="after the timed steps, time one offload of the cache's state to "
                          "pinned host memory and its restore into a new device buffer "
@@ -255,16 +258,20 @@ def main():
             for t in range(3):
                 src = torch.from_numpy(st[s][t])
                 dev[s][t][b, h].copy_(src.view(torch.bfloat16) if bf else src)
+    if args.layout == "bnhd":
+        dev = [[t.transpose(1, 2).contiguous() for t in step] for step in dev]
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     print(f"[bench] inputs staged in HBM: {S} steps x 3 x {B}x{H}x{N}x{D} {cfg.qkv_dtype} "
           f"({t_gen:.1f} s)", file=sys.stderr, flush=True)
 
     geom = dita.geometry_from(cfg)
+    geom.layout = dita.LAYOUT_BNHD if args.layout == "bnhd" else dita.LAYOUT_BHND
     # blocks that can ever be non-skip: the anchor step's active set
     act = (dita.dita_policy_mask(geom, dita.policy_from(cfg.policy(1).as_anchor())) != 0)
     cache = dita.Cache(geom, active_mask=act.astype(np.uint8))
-    out = torch.empty((B, H, N, D), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, N, H, D) if args.layout == "bnhd" else (B, H, N, D),
+                      dtype=torch.float32, device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     if args.policy == "planner":
         from workloads import Policy, PLANNER
@@ -360,9 +367,9 @@ def main():
     achieved = fresh_flops / launches / (avg_kernel_ms * 1e-3) / 1e12
     digest = kernel_source_digest()
     label = kernel_label(D, args.policy == "planner", cfg.cache_dtype == "fp8")
-    # the counter run covers the fixed schedule without merging (the same launch mix)
+    # the counter run covers the fixed schedule without merging, on [B, H, N, D] inputs
     traffic = measured_traffic(digest, label, cfg.name) \
-        if args.policy == "schedule" and not merge_sizes else None
+        if args.policy == "schedule" and not merge_sizes and args.layout == "bhnd" else None
     t_roof_sum = sum(w[0] / (PEAK_BF16_TFLOPS * 1e12) + (w[1] + w[2]) / (PEAK_HBM_GBS * 1e9)
                      for w in work)
     t_roof_max = sum(max(w[0] / (PEAK_BF16_TFLOPS * 1e12), (w[1] + w[2]) / (PEAK_HBM_GBS * 1e9))
@@ -385,7 +392,8 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "heads": H, "tokens": N, "head_dim": D,
                    "partitions": cfg.num_partitions, "denoise_steps": S,
                    "schedule": schedule_desc,
-                   "cache": f"{cfg.cache_dtype} O + f32 lse", "out": "f32"},
+                   "cache": f"{cfg.cache_dtype} O + f32 lse", "out": "f32",
+                   "layout": args.layout},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

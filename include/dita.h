@@ -29,7 +29,8 @@
  *     alive until the stream has passed the step.  A handle allocates pinned host memory
  *     of its own (plan uploads, the planner's read-back, merge jobs), released by
  *     dita_cache_free.
- *   - Q, K, V and out are contiguous [B, H, N, D] (row-major, D fastest).
+ *   - Q, K, V and out are contiguous [B, H, N, D] (row-major, D fastest), or [B, N, H, D]
+ *     with the geometry's layout BNHD.
  *   - A handle is not thread-safe; different handles are independent.
  */
 #ifndef DITA_H
@@ -65,6 +66,12 @@ typedef enum dita_dtype { DITA_F32 = 0, DITA_BF16 = 1, DITA_FP8_E4M3 = 2 } dita_
 
 enum { DITA_SKIP = 0, DITA_FRESH = 1, DITA_REUSE = 2 };
 
+/* Memory layout of Q, K, V and out (lse_out is always [B, H, N]):
+ *   BHND  [B, H, N, D], D fastest (a head's tokens contiguous);
+ *   BNHD  [B, N, H, D], D fastest (a token's heads contiguous: the layout of a fused QKV
+ *         projection's output, usable without a transpose). */
+typedef enum dita_layout { DITA_LAYOUT_BHND = 0, DITA_LAYOUT_BNHD = 1 } dita_layout;
+
 typedef enum dita_policy_kind {
   DITA_POLICY_EXPLICIT = 0,           /* mask given by the caller                            */
   DITA_POLICY_FRAME_THRESHOLD = 1,    /* FRESH iff |f_i - f_j| <= max_fresh_frame_dist       */
@@ -90,6 +97,8 @@ typedef struct dita_geometry {
   dita_dtype cache_o_dtype;                 /* qkv_dtype, or FP8_E4M3 with bf16 Q/K/V;
                                                cache lse is f32                             */
   float softmax_scale;                      /* tau; <= 0 selects 1/sqrt(D)                  */
+  int32_t layout;                           /* dita_layout of Q, K, V, out; zero-initialise
+                                               the struct for BHND                          */
 } dita_geometry;
 
 /* One step's block policy (DiTango, "Anchor-Guided Selection Planner"): which blocks are
@@ -224,9 +233,9 @@ dita_status dita_get_block_plan(const dita_cache* cache, uint8_t* mask, int32_t*
                                 int32_t* counts);
 
 /* Run one denoising step's attention on `hip_stream` (a hipStream_t; NULL = default).
- *   q, k, v   device, [B,H,N,D] of qkv_dtype (bf16: |v| <= 65504, see device_v_range_errors),
- *             16-byte aligned
- *   out       device, [B,H,N,D] f32: the merged output; 16-byte aligned, overlapping
+ *   q, k, v   device, [B,H,N,D] (or [B,N,H,D] with layout BNHD) of qkv_dtype (bf16: |v| <=
+ *             65504, see device_v_range_errors), 16-byte aligned
+ *   out       device, f32 in the same layout: the merged output; 16-byte aligned, overlapping
  *             neither q, k, v nor the cache buffer
  *   lse_out   device, [B,H,N] f32 natural-log L, or NULL; 4-byte aligned
  * Fresh blocks are recomputed and written back to their slots; reused blocks are read from

@@ -28,6 +28,8 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "SHAPE", 3: "UNSUPPORTED", 4:
                 5: "CACHE_MISS", 6: "BUFFER_TOO_SMALL", 7: "NO_POLICY", 8: "DEVICE",
                 9: "OFFLOADED"}
 F32, BF16, FP8_E4M3 = 0, 1, 2
+LAYOUT_BHND, LAYOUT_BNHD = 0, 1
+_LAYOUTS = {"bhnd": LAYOUT_BHND, "bnhd": LAYOUT_BNHD}
 _DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 SKIP, FRESH, REUSE = 0, 1, 2
 POLICY_EXPLICIT, POLICY_FRAME_THRESHOLD, POLICY_FRESH_BUDGET, POLICY_CENTROID_THRESHOLD = 0, 1, 2, 3
@@ -55,7 +57,7 @@ class Geometry(ctypes.Structure):
                 ("grid_w", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("partition_offsets", ctypes.POINTER(ctypes.c_int32)),
                 ("qkv_dtype", ctypes.c_int32), ("cache_o_dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("layout", ctypes.c_int32)]
 
 
 class BlockPolicy(ctypes.Structure):
@@ -131,9 +133,11 @@ def _u8(arr):
 
 
 def make_geometry(batch, heads, tokens, head_dim, frames, grid_h, grid_w, num_partitions,
-                  dtype="bf16", offsets=None, softmax_scale=0.0, cache_dtype=None):
+                  dtype="bf16", offsets=None, softmax_scale=0.0, cache_dtype=None,
+                  layout="bhnd"):
     """A Geometry; `offsets` (P+1 ints) or None for the array_split rule; `cache_dtype`
-    (cached O) defaults to `dtype` ("fp8" = e4m3, with bf16 Q/K/V)."""
+    (cached O) defaults to `dtype` ("fp8" = e4m3, with bf16 Q/K/V); `layout` of Q, K, V and
+    out: "bhnd" ([B, H, N, D]) or "bnhd" ([B, N, H, D])."""
     g = Geometry()
     g.batch, g.heads, g.tokens, g.head_dim = batch, heads, tokens, head_dim
     g.frames, g.grid_h, g.grid_w, g.num_partitions = frames, grid_h, grid_w, num_partitions
@@ -143,6 +147,7 @@ def make_geometry(batch, heads, tokens, head_dim, frames, grid_h, grid_w, num_pa
     g.qkv_dtype = dt
     g.cache_o_dtype = cd
     g.softmax_scale = softmax_scale
+    g.layout = _LAYOUTS[layout] if isinstance(layout, str) else int(layout)
     if offsets is not None:
         arr = (ctypes.c_int32 * len(offsets))(*[int(x) for x in offsets])
         g._offsets_keepalive = arr
@@ -287,6 +292,8 @@ class Cache:
                 raise ValueError("q, k, v must be contiguous [B, H, N, D]")
         g = self.geom
         shape = (g.batch, g.heads, g.tokens, g.head_dim)
+        if g.layout == LAYOUT_BNHD:
+            shape = (g.batch, g.tokens, g.heads, g.head_dim)
         if tuple(q.shape) != shape or tuple(k.shape) != shape or tuple(v.shape) != shape:
             raise ValueError(f"q, k, v must have shape {shape}")
         want = torch.bfloat16 if g.qkv_dtype == BF16 else torch.float32
@@ -295,7 +302,8 @@ class Cache:
         if out is None:
             out = torch.empty(shape, dtype=torch.float32, device=q.device)
         if lse is None and want_lse:
-            lse = torch.empty(shape[:3], dtype=torch.float32, device=q.device)
+            lse = torch.empty((g.batch, g.heads, g.tokens), dtype=torch.float32,
+                              device=q.device)
         _check(_lib.dita_attn_step(self._h, _P(q.data_ptr()), _P(k.data_ptr()),
                                    _P(v.data_ptr()), _P(out.data_ptr()),
                                    _P(lse.data_ptr()) if lse is not None else None,

@@ -47,6 +47,7 @@ struct Geo {
   int B = 0, H = 0, N = 0, D = 0, DP = 0, P = 0;
   int frames = 0, gh = 0, gw = 0, F = 0;
   dita_dtype qkv = DITA_BF16, cache_o = DITA_BF16;
+  int layout = DITA_LAYOUT_BHND;
   float tau = 0.f;
   std::vector<int32_t> offs;    // P+1
   std::vector<int64_t> c2;      // doubled centroids
@@ -89,6 +90,10 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
                 "bf16 Q/K/V");
   r.qkv = g->qkv_dtype;
   r.cache_o = g->cache_o_dtype;
+  if (g->layout != DITA_LAYOUT_BHND && g->layout != DITA_LAYOUT_BNHD)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "unknown layout %d", g->layout);
+  r.layout = g->layout;
+  if ((int64_t)r.H * r.D > INT32_MAX) return fail(DITA_ERR_SHAPE, "heads x head_dim too large");
   if (r.bf16()) {
     r.DP = dita::bf16_padded_dim(r.D);
     if (!r.DP) return fail(DITA_ERR_UNSUPPORTED, "bf16 head_dim must be a multiple of 8 <= 128");
@@ -567,6 +572,11 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->off_rows = a->off_tail + 2 * g.num_tail_wg;
   a->off_ent = a->off_rows + 4 * P;
   a->B = g.B; a->H = g.H; a->N = g.N; a->D = g.D; a->DP = g.DP; a->P = P;
+  if (g.layout == DITA_LAYOUT_BNHD) {
+    a->sB = (int64_t)g.N * g.H * g.D; a->sH = g.D; a->ld = g.H * g.D;
+  } else {
+    a->sB = (int64_t)g.H * g.N * g.D; a->sH = (int64_t)g.N * g.D; a->ld = g.D;
+  }
   a->num_tiles = g.num_tiles;
   a->num_slots = c->num_slots;
   a->slot_rows = g.slot_rows;

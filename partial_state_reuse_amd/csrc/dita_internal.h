@@ -64,6 +64,10 @@ struct StepArgs {
   const int32_t* plan;       // device plan (layout above)
   int32_t off_offs, off_poffs, off_tiles, off_tail, off_rows, off_ent;
   int32_t B, H, N, D, DP, P;
+  // element strides of Q, K, V and out: (b, h, token n, d) at b*sB + h*sH + n*ld + d
+  // ([B,H,N,D]: sB = H N D, sH = N D, ld = D; [B,N,H,D]: sB = N H D, sH = D, ld = H D)
+  int64_t sB, sH;
+  int32_t ld;
   int32_t num_tiles;         // workgroup tiles per (b, h)
   int32_t num_slots;
   int32_t slot_rows;

@@ -59,6 +59,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// element offset of head (b, h) = (bh / H, bh % H) in Q, K, V and out
+__device__ __forceinline__ size_t head_base(const StepArgs& a, int bh) {
+  const int b = bh / a.H, h = bh - b * a.H;
+  return (size_t)b * a.sB + (size_t)h * a.sH;
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // max / sum of the values held by lanes l and l^32, in every lane, through ds_bpermute with
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
   const int p = lo;
   const int o_p = offs[p], n_p = offs[p + 1] - o_p;
   const int k0 = col0 - poffs[p];      // first key (partition-relative)
-  const uint16_t* V = (const uint16_t*)a.v + (size_t)bh * a.N * a.D;
+  const uint16_t* V = (const uint16_t*)a.v + head_base(a, bh);
   // load 64 keys x D (8 elements per 16-byte chunk), converting to fp16
   const int cpr = a.D / 8;             // chunks per row
   int out_of_range = 0;
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(256) void transpose_v(StepArgs a) {
     const int r = c / cpr, d8 = (c - r * cpr) * 8;
     const int key = k0 + r;
     u32x4 val = {0u, 0u, 0u, 0u};
-    if (key < n_p) val = ld16(V + (size_t)(o_p + key) * a.D + d8);
+    if (key < n_p) val = ld16(V + (size_t)(o_p + key) * a.ld + d8);
     const bf16x8 b = as_bf16x8(val);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -380,7 +386,7 @@ __device__ __forceinline__ void finish_rows(const StepArgs& a, int bh, int o_i, 
   const size_t bhN = (size_t)bh * a.N;
   if (myrow < n_i) {
     const float inv = 1.0f / l_row;
-    float* orow = a.out + (bhN + o_i + myrow) * a.D;
+    float* orow = a.out + head_base(a, bh) + (size_t)(o_i + myrow) * a.ld;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -433,7 +439,6 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
   const cint* rinfo = plan + a.off_rows + 4 * i;
   const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
   const cint* ent = plan + a.off_ent;
-  const size_t bhN = (size_t)bh * a.N;
   const float sc = a.scale_log2;
   const float inv_sc = 1.0f / sc;
   const int paddr = partner_addr();
@@ -441,13 +446,13 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
 
   bf16x8 qf[NKC];
   {
-    const uint16_t* Q = (const uint16_t*)a.q + bhN * a.D;
+    const uint16_t* Q = (const uint16_t*)a.q + head_base(a, bh);
     const bool ok = myrow < n_i;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int d0 = kc * 16 + h32 * 8;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok && d0 < a.D) v = ld16(Q + (size_t)(o_i + myrow) * a.D + d0);
+      if (ok && d0 < a.D) v = ld16(Q + (size_t)(o_i + myrow) * a.ld + d0);
       qf[kc] = as_bf16x8(v);
     }
   }
@@ -457,7 +462,7 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
   float m_row = kNegInf, l_row = 0.f;
   const size_t slot_elems = (size_t)a.slot_rows * DP;
   typename CacheElem<FP8>::type* cache_o = (typename CacheElem<FP8>::type*)a.cache_o;
-  const uint16_t* Kg = (const uint16_t*)a.k + bhN * a.D;
+  const uint16_t* Kg = (const uint16_t*)a.k + head_base(a, bh);
   const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
 
   // ---------------- fresh blocks ----------------
@@ -474,7 +479,7 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
       bf16x8 kf[NKC];
       {
         const int key = min(kbase + key_of_row(l32), n_j - 1);
-        const uint16_t* src = Kg + (size_t)(o_j + key) * a.D;
+        const uint16_t* src = Kg + (size_t)(o_j + key) * a.ld;
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) kf[kc] = as_bf16x8(ld16(src + min(kc * 16 + h32 * 8, a.D - 8)));
       }
@@ -621,7 +626,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const cint* rinfo = plan + a.off_rows + 4 * i;
   const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
   const cint* ent = plan + a.off_ent;
-  const size_t bhN = (size_t)bh * a.N;
   const float sc = a.scale_log2;
   const float inv_sc = 1.0f / sc;
   const int paddr = partner_addr();
@@ -630,13 +634,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of query row l%32 per chunk
   bf16x8 qf[NKC];
   {
-    const uint16_t* Q = (const uint16_t*)a.q + bhN * a.D;
+    const uint16_t* Q = (const uint16_t*)a.q + head_base(a, bh);
     const bool ok = myrow < n_i;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int d0 = kc * 16 + h32 * 8;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok && d0 < a.D) v = ld16(Q + (size_t)(o_i + myrow) * a.D + d0);
+      if (ok && d0 < a.D) v = ld16(Q + (size_t)(o_i + myrow) * a.ld + d0);
       qf[kc] = as_bf16x8(v);
     }
   }
@@ -649,7 +653,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
 
   const size_t slot_elems = (size_t)a.slot_rows * DP;
   typename CacheElem<FP8>::type* cache_o = (typename CacheElem<FP8>::type*)a.cache_o;
-  const uint16_t* Kg = (const uint16_t*)a.k + bhN * a.D;
+  const uint16_t* Kg = (const uint16_t*)a.k + head_base(a, bh);
   const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
 
   // ---------------- fresh blocks ----------------
@@ -675,7 +679,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
         const int c = tid + 256 * m;
         const int r = c / (DP / 8), d8 = (c % (DP / 8)) * 8;
         const int key = min(kt * KT + r, n_j - 1);
-        pk[m] = ld16(Kg + (size_t)(o_j + key) * a.D + min(d8, a.D - 8));
+        pk[m] = ld16(Kg + (size_t)(o_j + key) * a.ld + min(d8, a.D - 8));
       }
 #pragma unroll
       for (int m = 0; m < CHV; ++m) {
@@ -798,14 +802,16 @@ __global__ __launch_bounds__(64) void step_f32(StepArgs a) {
   const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
   const int* ent = plan + a.off_ent;
   const size_t bhN = (size_t)bh * a.N;
-  const float* Q = (const float*)a.q + bhN * D;
-  const float* K = (const float*)a.k + bhN * D;
-  const float* V = (const float*)a.v + bhN * D;
+  const size_t hb = head_base(a, bh);
+  const int ld = a.ld;
+  const float* Q = (const float*)a.q + hb;
+  const float* K = (const float*)a.k + hb;
+  const float* V = (const float*)a.v + hb;
   float* cache_o = (float*)a.cache_o;
 
   float q[DP];
 #pragma unroll
-  for (int d = 0; d < DP; ++d) q[d] = (ok && d < D) ? Q[(size_t)(o_i + r) * D + d] : 0.f;
+  for (int d = 0; d < DP; ++d) q[d] = (ok && d < D) ? Q[(size_t)(o_i + r) * ld + d] : 0.f;
   float acc[DP];
 #pragma unroll
   for (int d = 0; d < DP; ++d) acc[d] = 0.f;
@@ -825,8 +831,8 @@ __global__ __launch_bounds__(64) void step_f32(StepArgs a) {
 #pragma unroll 4
       for (int d = 0; d < DP; ++d) {
         const bool kv = key < n_j && d < D;
-        sK[lane][d] = kv ? K[(size_t)(o_j + key) * D + d] : 0.f;
-        sV[lane][d] = kv ? V[(size_t)(o_j + key) * D + d] : 0.f;
+        sK[lane][d] = kv ? K[(size_t)(o_j + key) * ld + d] : 0.f;
+        sV[lane][d] = kv ? V[(size_t)(o_j + key) * ld + d] : 0.f;
       }
       __syncthreads();
       const int nk = n_j - c0 < KB ? n_j - c0 : KB;
@@ -892,7 +898,7 @@ __global__ __launch_bounds__(64) void step_f32(StepArgs a) {
     m_row = mn;
   }
   if (ok) {
-    float* orow = a.out + (bhN + o_i + r) * D;
+    float* orow = a.out + hb + (size_t)(o_i + r) * ld;
 #pragma unroll
     for (int d = 0; d < DP; ++d)
       if (d < D) orow[d] = acc[d] / l_row;

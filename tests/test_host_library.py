@@ -262,3 +262,26 @@ def test_offload_size_and_argument_errors(idx, cache):
     assert lib.dita_cache_offload_bytes(None, ctypes.byref(size)) == 1
     assert lib.dita_cache_offload_bytes(c._h, None) == 1
     c.free()
+
+
+def test_layout_field():
+    """The layout of Q, K, V and out changes neither the buffer size nor the plan; an unknown
+    layout is rejected before anything else."""
+    cfg = CONFIGS[3]
+    g1 = dita.geometry_from(cfg)
+    g2 = dita.geometry_from(cfg)
+    g2.layout = dita.LAYOUT_BNHD
+    assert dita.dita_cache_required_bytes(g1) == dita.dita_cache_required_bytes(g2)
+    plans = []
+    for g in (g1, g2):
+        n = dita.dita_cache_required_bytes(g)
+        c = dita.Cache(g, buffer_ptr=FAKE, buffer_bytes=n)
+        c.set_policy(dita.policy_from(cfg.policy(1)))
+        plans.append(c.plan())
+        c.free()
+    assert all(np.array_equal(plans[0][k], plans[1][k]) for k in plans[0])
+    g3 = dita.geometry_from(cfg)
+    g3.layout = 2
+    with pytest.raises(dita.DitaError) as e:
+        dita.dita_cache_required_bytes(g3)
+    assert e.value.name == "INVALID_ARGUMENT"
