@@ -285,3 +285,33 @@ def test_layout_field():
     with pytest.raises(dita.DitaError) as e:
         dita.dita_cache_required_bytes(g3)
     assert e.value.name == "INVALID_ARGUMENT"
+
+
+def test_header_is_c_and_matches_the_binding(tmp_path):
+    """include/dita.h compiles as plain C99, and its structs have the sizes and field offsets
+    the ctypes binding declares (a mismatch would pass wrong arguments silently)."""
+    import ctypes
+    import shutil
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    structs = {"dita_geometry": dita.Geometry, "dita_block_policy": dita.BlockPolicy,
+               "dita_step_stats": dita.StepStats}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "dita.h"',
+             'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "abi.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "abi"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-I",
+                    os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(line.rsplit(" ", 1) for line in
+               subprocess.run([str(exe)], capture_output=True, text=True, check=True)
+               .stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert int(got[f"{cname}.{fname}"]) == getattr(py, fname).offset, (cname, fname)
