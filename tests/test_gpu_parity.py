@@ -38,9 +38,10 @@ def active_for(cfg):
 
 
 def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offsets=None,
-                  check_slots=True, modify=None, recomputes=None):
+                  check_slots=True, modify=None, recomputes=None, layout="bhnd"):
     """Run every step on the GPU and compare with the oracle on `heads` (and `rows`).
 
+    layout      "bhnd", or "bnhd": Q, K, V and out handed to the library as [B, N, H, D]
     modify      optional callable(dev, kept) that edits the device inputs and the host copies
                 of `heads` alike before the run
     recomputes  None, 0 (no fresh block may be computed a second time after its cached lse
@@ -54,6 +55,8 @@ def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offset
     if modify is not None:
         modify(dev, kept)
     g = dita.geometry_from(cfg, offsets=offsets)
+    if layout == "bnhd":
+        g.layout = dita.LAYOUT_BNHD
     cache = dita.Cache(g, active_mask=active_for(cfg) if offsets is None else None)
     pols = policies or [cfg.policy(s) for s in range(1, S + 1)]
     outs = []
@@ -62,7 +65,11 @@ def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offset
         cache.set_policy(dita.policy_from(pols[s]))
         plans.append(cache.plan())
         q, k, v = dev[s]
+        if layout == "bnhd":
+            q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
         out, lse = cache.step(q, k, v)
+        if layout == "bnhd":
+            out = out.transpose(1, 2)
         sel = torch.as_tensor(rows, device=out.device) if rows is not None else None
         per_head = {}
         for (b, h) in heads:
@@ -202,9 +209,11 @@ def _sweep_case(seed):
 
 @pytest.mark.parametrize("seed", range(48))
 def test_random_geometry_sweep(dita, seed):
-    """Random small workloads, every element and every step against the oracle."""
+    """Random small workloads, every element and every step against the oracle; odd seeds
+    hand Q, K, V and out over as [B, N, H, D]."""
     cfg = _sweep_case(seed)
-    run_and_check(dita, cfg, heads=[(0, h) for h in range(cfg.heads)])
+    run_and_check(dita, cfg, heads=[(0, h) for h in range(cfg.heads)],
+                  layout="bnhd" if seed % 2 else "bhnd")
 
 
 def test_explicit_masks_and_custom_offsets_bf16(dita):
