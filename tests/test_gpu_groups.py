@@ -82,25 +82,28 @@ def ulp(x, bf16):
 
 def merge_rounding_bar(r, offs, P, resolved, inputs, step, bf16):
     """Extra output allowance [N, D] at 0-based step `step` for the merged states read there:
-    w_r * levels * ulp(max |V| over the group's keys and the steps so far) / 2."""
+    w_r * levels_r * ulp(max |V| over the group's keys and the steps so far) / 2, where
+    levels_r counts the merge levels (group sizes g) that merged something into the state
+    read at (i, j): a member without a state of its own in the same g-group."""
     levels = [g for t, lst in resolved.items() if t <= step for (g, _) in lst]
     extra = np.zeros((offs[-1], inputs[0][2].shape[1]))
     if not levels:
         return extra
-    G = max(levels)
     vmax = [max(float(np.abs(inputs[t][2][offs[j]:offs[j + 1]]).max()) for t in range(step + 1))
             for j in range(P)]
     for i in range(P):
         rows = slice(offs[i], offs[i + 1])
+        covered = [m for m in range(P) if r.mask[i, m] == 2 and (i, m) not in r.block_o]
         for j in range(P):
             if r.mask[i, j] != 2 or (i, j) not in r.block_o:
                 continue
-            group = [m for m in range(P) if m // G == j // G]
-            if not any(m != j and r.mask[i, m] == 2 and (i, m) not in r.block_o for m in group):
+            mine = [g for g in levels if any(m // g == j // g for m in covered)]
+            if not mine:
                 continue                                   # not a merged state
+            members = {m for g in mine for m in range(P) if m // g == j // g}
             w = np.exp(r.block_lse[(i, j)] - r.lse[rows])
-            vm = max(vmax[m] for m in group)
-            extra[rows] += (w * len(levels) * 0.5 * float(ulp(vm, bf16)))[:, None]
+            vm = max(vmax[m] for m in members)
+            extra[rows] += (w * len(mine) * 0.5 * float(ulp(vm, bf16)))[:, None]
     return extra
 
 

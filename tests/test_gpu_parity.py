@@ -86,7 +86,12 @@ def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offset
     st = cache.stats()
     ok_all = True
     worst = (0.0, 0.0)
+    offs_used = oracle.partition_offsets(cfg.tokens, cfg.num_partitions) \
+        if offsets is None else offsets
+    n_max = int(np.max(np.diff(np.asarray(offs_used))))
     for (b, h) in heads:
+        # f32: the bar for blocks of this length (gpu_helpers.f32_bar)
+        f32_max = gh.f32_bar(n_max, max(float(np.abs(x[2]).max()) for x in kept[(b, h)][:S]))
         # the bar is against fp64 (no cache rounding); the reference that also rounds its
         # cache to the workload's precision must agree on average
         ref = oracle.run_head(cfg, b, h, steps=S, rows=rows, policies=pols,
@@ -103,7 +108,7 @@ def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offset
             assert np.array_equal(p["reuse_cols"], r.reuse_cols)
             assert np.array_equal(p["counts"], r.counts)
             o, l = outs[s][(b, h)]
-            ok, mx, mean = compare(o, r.out, bf, f"  b={b} h={h} step {s + 1} out")
+            ok, mx, mean = compare(o, r.out, bf, f"  b={b} h={h} step {s + 1} out", f32_max)
             worst = (max(worst[0], mx), max(worst[1], mean))
             ok_all &= ok
             emean = float(np.mean(np.abs(o - emu[s].out)))
@@ -120,7 +125,8 @@ def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offset
                 O_ref, l_ref = oracle.block_state(Qs[sl_i], Ks[sl_j], Vs[sl_j],
                                                   1.0 / np.sqrt(cfg.head_dim))
                 rnd = oracle.round_bf16 if bf else oracle.round_f32
-                ok = gh.compare_cached(o_slot, rnd(O_ref), O_ref, bf, f"  cached state ({i},{j})")
+                ok = gh.compare_cached(o_slot, rnd(O_ref), O_ref, bf, f"  cached state ({i},{j})",
+                                       f32_max)
                 assert ok, f"slot ({i},{j})"
                 assert np.max(np.abs(l_slot - l_ref)) < (2e-3 if bf else 1e-5)
     bh = cfg.batch * cfg.heads
