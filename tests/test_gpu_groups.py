@@ -56,7 +56,7 @@ def test_group_composition(dita, case):
     run_group_case(dita, case)
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", list(range(48)) + [1357])
 def test_group_composition_sweep(dita, seed):
     """Random small workloads (3-8 frames, 3-10 x 3-16 grid, 3-10 partitions, head dim, path)
     with a random group size merged after the anchor (every eligible group, or the groups
