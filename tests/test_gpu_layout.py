@@ -29,6 +29,7 @@ CASES = [
     ("layout-bf16-d72", 1, 3, 8, 10, 5, 72, 2, 3, "bf16"),
     ("layout-bf16-d128", 1, 3, 8, 10, 6, 128, 2, 3, "bf16"),
     ("layout-f32-d64", 2, 4, 4, 6, 4, 64, 3, 2, "f32"),
+    ("layout-bf16-d64-16heads", 1, 4, 10, 26, 8, 64, 16, 2, "bf16"),  # token stride 1024
 ]
 
 
