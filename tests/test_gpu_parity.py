@@ -168,6 +168,8 @@ RAGGED_CASES = [
     ("tiny-partitions-d64", 1, 3, 11, 11, 64, 1, 3, "budget"),
     ("tile-sparse-d64", 6, 5, 7, 6, 64, 2, 4, "tile"),
     ("video-slice-d64", 2, 45, 80, 8, 64, 2, 3, "budget"),
+    ("many-partitions-d64", 4, 16, 16, 256, 64, 1, 2, "tile"),     # 4-row partitions
+    ("max-partitions-d64", 4, 16, 16, 1024, 64, 1, 2, "budget"),   # 1024 one-row partitions
 ]
 
 
