@@ -38,6 +38,17 @@ def fp8_delta_rtol(n):
     return max(1e-2, 1.0 / np.sqrt(n))
 
 
+def bf16_delta_rtol(n):
+    """Relative bar on the growth with a bf16 cache, over an RMS of n elements.  The same
+    rounding noise as with fp8, at bf16's spacing (1/256 to 1/128 of the value): an element
+    landing one spacing apart moves its squared change by about twice the change times the
+    spacing.  With the state about ten times its per-step change and, at worst, every element
+    moved so in a random direction, one standard deviation of the RMS's relative error is
+    about 10/(128 sqrt(n)); the bar is three of them, 0.25/sqrt(n), and never under 5e-3
+    (which it exceeds for partitions of under 2500 elements)."""
+    return max(DELTA_RTOL["bf16"], 0.25 / np.sqrt(n))
+
+
 @pytest.fixture(scope="module")
 def dita():
     import partial_state_reuse_amd as d
@@ -55,6 +66,9 @@ CASES = [
     ("planner-f32", 3, 4, 8, 6, 64, 2, 6, "f32", 60, 2, 0, 0.0, False),
     # fp8 state cache: decisions and measurements (its outputs are checked in test_gpu_fp8)
     ("planner-fp8-cache", 4, 6, 10, 8, 64, 2, 6, "bf16/fp8", 60, 1, 3, 0.0, False),
+    # many partitions: 4-row and 8-row partitions, P x P plans of 64K and 16K blocks
+    ("planner-bf16-256-partitions", 4, 16, 16, 256, 64, 1, 5, "bf16", 60, 1, 3, 0.0, False),
+    ("planner-fp8-128-partitions", 4, 16, 16, 128, 64, 1, 4, "bf16/fp8", 60, 2, 0, 0.0, True),
 ]
 
 
@@ -167,10 +181,12 @@ def run_planner_case(dita, case, modify=None, recomputes=None, require_reuse=Tru
             got = st["delta"][s - 1]
             rel = np.abs(got - ref.delta) / np.maximum(ref.delta, 1e-12)
             log(f"step {s}: growth {np.round(got, 5).tolist()} rel err max {rel.max():.2e}")
+            rows = np.diff(np.asarray(offs, np.int64))
+            sizes = [len(heads) * int(rows[i]) * cfg.head_dim for i in range(P)]
             if cdt == "fp8":
-                rows = np.diff(np.asarray(offs, np.int64))
-                bar = np.array([fp8_delta_rtol(len(heads) * int(rows[i]) * cfg.head_dim)
-                                for i in range(P)])
+                bar = np.array([fp8_delta_rtol(n) for n in sizes])
+            elif cdt == "bf16":
+                bar = np.array([bf16_delta_rtol(n) for n in sizes])
             else:
                 bar = DELTA_RTOL[cdt]
             assert np.all(rel <= bar), f"step {s}: growth rel err {rel.max():.3e}"
