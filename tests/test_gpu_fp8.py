@@ -57,6 +57,7 @@ CASES = [
     ("fp8-d128", 3, 8, 10, 6, 128, 2, 4, "frame", None),
     ("fp8-d72", 2, 9, 11, 3, 72, 2, 3, "frame", None),
     ("fp8-d64-merged", 8, 5, 7, 8, 64, 1, 4, "frame", {1: [(2, None)]}),
+    ("fp8-d64-256-partitions", 4, 16, 16, 256, 64, 1, 3, "budget", None),   # 4-row partitions
 ]
 
 

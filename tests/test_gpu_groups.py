@@ -37,6 +37,8 @@ CASES = [
     ("groups-bf16-d128-all", 8, 4, 6, 8, 128, 1, 4, "bf16", {1: [(2, None)]}),
     ("groups-bf16-d72-ragged", 6, 5, 7, 6, 72, 1, 4, "bf16", {1: [(3, "sel")], 2: [(6, None)]}),
     ("groups-f32", 8, 2, 4, 8, 64, 2, 5, "f32", {2: [(2, "sel")]}),
+    ("groups-bf16-128-partitions", 4, 16, 16, 128, 64, 1, 4, "bf16",
+     {1: [(8, "sel")], 2: [(32, None)]}),                       # 8-row partitions
 ]
 
 
