@@ -351,16 +351,21 @@ def test_error_paths_on_device(dita):
 # --------------------------------------------------------------------------------------
 # full-size workloads, sampled rows
 # --------------------------------------------------------------------------------------
-def _full(dita, idx, heads, per_part):
+def _full(dita, idx, heads, per_part, layout="bhnd"):
     from oracle.policy import partition_offsets
     cfg = CONFIGS[idx]
     rows = gh.sample_rows(partition_offsets(cfg.tokens, cfg.num_partitions), per_part,
                           np.random.default_rng(idx))
-    run_and_check(dita, cfg, heads=heads, rows=rows, recomputes=0)
+    run_and_check(dita, cfg, heads=heads, rows=rows, recomputes=0, layout=layout)
 
 
 def test_full_video29f_720p(dita):
     _full(dita, 3, heads=[(0, 0), (0, 13), (0, 23)], per_part=12)
+
+
+def test_full_video29f_720p_token_major(dita):
+    """The same workload with Q, K, V and out as [B, N, H, D] (a token stride of H D = 1536)."""
+    _full(dita, 3, heads=[(0, 5), (0, 18)], per_part=8, layout="bnhd")
 
 
 def test_full_video93f_tile_sparse(dita):
