@@ -33,6 +33,8 @@ CASES = [
     ("offload-fp8-merged", 6, 4, 6, 6, 64, 1, 5, "bf16", "fp8", "schedule", [2], {1: 2}),
     ("offload-f32", 4, 4, 6, 4, 64, 2, 3, "f32", "f32", "schedule", [1], {}),
     ("offload-planner", 6, 5, 7, 6, 64, 2, 5, "bf16", "bf16", "planner", [1, 2, 3], {}),
+    ("offload-planner-fp8-128-partitions", 4, 16, 16, 128, 64, 1, 4, "bf16", "fp8", "planner",
+     [1, 2], {}),
 ]
 
 
