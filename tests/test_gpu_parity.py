@@ -170,6 +170,8 @@ RAGGED_CASES = [
     ("video-slice-d64", 2, 45, 80, 8, 64, 2, 3, "budget"),
     ("many-partitions-d64", 4, 16, 16, 256, 64, 1, 2, "tile"),     # 4-row partitions
     ("max-partitions-d64", 4, 16, 16, 1024, 64, 1, 2, "budget"),   # 1024 one-row partitions
+    ("many-partitions-d72", 4, 16, 16, 128, 72, 1, 2, "frame"),     # 8-row partitions
+    ("many-partitions-d128", 4, 16, 16, 200, 128, 1, 3, "budget"),  # 5- and 6-row partitions
 ]
 
 
