@@ -38,14 +38,16 @@ def active_for(cfg):
 
 
 def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offsets=None,
-                  check_slots=True, modify=None, recomputes=None, layout="bhnd"):
+                  check_slots=True, modify=None, recomputes=None, layout="bhnd",
+                  expect_f32_bar=None):
     """Run every step on the GPU and compare with the oracle on `heads` (and `rows`).
 
     layout      "bhnd", or "bnhd": Q, K, V and out handed to the library as [B, N, H, D]
     modify      optional callable(dev, kept) that edits the device inputs and the host copies
                 of `heads` alike before the run
     recomputes  None, 0 (no fresh block may be computed a second time after its cached lse
-                was rejected as the softmax reference) or "some" (at least one must be)"""
+                was rejected as the softmax reference) or "some" (at least one must be)
+    expect_f32_bar  f32 workloads: the max-abs bar every head must be held to (checked)"""
     oracle = oracle_mod()
     S = steps or cfg.steps
     bf = cfg.qkv_dtype == "bf16"
@@ -92,6 +94,8 @@ def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offset
     for (b, h) in heads:
         # f32: the bar for blocks of this length (gpu_helpers.f32_bar)
         f32_max = gh.f32_bar(n_max, max(float(np.abs(x[2]).max()) for x in kept[(b, h)][:S]))
+        if expect_f32_bar is not None and not bf:
+            assert f32_max == expect_f32_bar, (f32_max, expect_f32_bar)
         # the bar is against fp64 (no cache rounding); the reference that also rounds its
         # cache to the workload's precision must agree on average
         ref = oracle.run_head(cfg, b, h, steps=S, rows=rows, policies=pols,
@@ -150,13 +154,16 @@ def run_and_check(dita, cfg, heads, rows=None, steps=None, policies=None, offset
 # small geometries: every element
 # --------------------------------------------------------------------------------------
 def test_tiny_f32_workload_all_heads(dita):
+    """The small fp32 workload (64-key blocks) is held to exactly the stated 1e-5."""
     cfg = CONFIGS[1]
-    run_and_check(dita, cfg, heads=[(0, 0), (0, 1)])
+    assert gh.f32_bar(64, 100.0) == 1e-5
+    run_and_check(dita, cfg, heads=[(0, 0), (0, 1)], expect_f32_bar=1e-5)
 
 
 def test_image_bf16_d72_workload(dita):
+    """Every head of the image workload, every element."""
     cfg = CONFIGS[2]
-    run_and_check(dita, cfg, heads=[(0, 0), (0, 9), (0, 15)])
+    run_and_check(dita, cfg, heads=[(0, h) for h in range(cfg.heads)])
 
 
 RAGGED_CASES = [

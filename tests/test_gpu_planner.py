@@ -77,6 +77,59 @@ def test_planner_schedule(dita, case):
     run_planner_case(dita, case)
 
 
+# Relative gap between the last block group chosen fresh and the first one reused, below which
+# the device's and the oracle's own measurements could order two groups differently: each
+# predicted error is importance (relative error <= 2e-4) times summed growth (<= 5e-3), so two
+# errors closer than twice that sum may swap.  The bar keeps a factor of two above it.
+FREE_RUN_MARGIN = 2e-2
+
+FREE_RUN_CASES = [
+    ("planner-free-d128", 3, 8, 10, 6, 128, 2, 5, "bf16", 60, 1, 3, 0.0, False),
+    ("planner-free-groups", 8, 5, 6, 8, 64, 2, 6, "bf16", 60, 2, 0, 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", FREE_RUN_CASES, ids=[c[0] for c in FREE_RUN_CASES])
+def test_planner_free_running_against_oracle(dita, case):
+    """The oracle's planner deciding from its own measurements (no masks handed to it) takes
+    the device's decisions at every step, on cases whose decision margins exceed what the
+    measurement tolerances could move (asserted from the oracle's own predicted errors)."""
+    run_planner_case(dita, case, free_running=True)
+
+
+def decision_margins(offs, frame_tokens, pol, E, valid):
+    """Per query group, the relative gap (e_k - e_{k+1}) / e_k between the last group chosen
+    fresh by error and the first one reused, where the budget cuts the ranking; groups forced
+    fresh do not take part.  A cut between two errors that are both exactly zero is exact on
+    both sides and is left out."""
+    from oracle.policy import active_mask
+    P = len(offs) - 1
+    act = active_mask(offs, frame_tokens, pol.tile_sparse)
+    G = max(1, pol.group_size or 1)
+    groups = [list(range(g0, min(P, g0 + G))) for g0 in range(0, P, G)]
+    out = []
+    for I, gi in enumerate(groups):
+        cand = []
+        for J, gj in enumerate(groups):
+            mem = [(i, j) for i in gi for j in gj if act[i, j]]
+            if not mem:
+                continue
+            e = sum(float(E[i, j]) for (i, j) in mem if i != j)
+            forced = J == I or any(not valid[i, j] for (i, j) in mem) or \
+                (pol.max_error > 0 and e > pol.max_error)
+            cand.append((J, e, forced))
+        A = len(cand)
+        n_reuse = min((pol.reuse_percent * A + 50) // 100, A - 1)
+        free = sorted([c for c in cand if not c[2]], key=lambda c: (-c[1], c[0]))
+        k = max(0, A - n_reuse - sum(c[2] for c in cand))
+        if 0 < k < len(free):
+            a, b = free[k - 1][1], free[k][1]
+            if a == 0.0 and b == 0.0:
+                continue
+            out.append((a - b) / a)
+    return out
+
+
 @pytest.mark.parametrize("seed", list(range(48)) + [103])
 def test_planner_sweep(dita, seed):
     """Random small workloads under the planner: geometry (2-6 frames, 3-12 x 3-20 grid, 3-10
@@ -117,7 +170,8 @@ def test_planner_measures_through_a_second_pass(dita):
     run_planner_case(dita, case, modify=modify, recomputes="some")
 
 
-def run_planner_case(dita, case, modify=None, recomputes=None, require_reuse=True):
+def run_planner_case(dita, case, modify=None, recomputes=None, require_reuse=True,
+                     free_running=False):
     import oracle
     from oracle.policy import active_mask, partition_offsets, FRESH, SKIP
     name, T, gh_, gw, P, D, H, S, dt, pct, G, period, cap, tile = case
@@ -151,6 +205,13 @@ def run_planner_case(dita, case, modify=None, recomputes=None, require_reuse=Tru
     elif recomputes == 0:
         assert recomputed == 0
 
+    # the last-fresh steps the library reports, against those the recorded masks imply
+    fs = np.zeros((P, P), dtype=np.int64)
+    for s in range(1, S + 1):
+        fs[masks[s - 1] == FRESH] = s
+        assert np.array_equal(states[s - 1]["fresh_step"], fs), f"step {s}: fresh_step"
+        assert states[s - 1]["steps"] == s
+
     # decisions, bit for bit
     n_reuse_steps = 0
     for s in range(1, S + 1):
@@ -168,6 +229,26 @@ def run_planner_case(dita, case, modify=None, recomputes=None, require_reuse=Tru
     if require_reuse:
         assert n_reuse_steps > 0
     log(f"decisions: {S} steps equal, {n_reuse_steps} with reuse")
+
+    if free_running:
+        # the oracle deciding from its own measurements
+        own = oracle.run_planner(cfg, heads, pol, cache_mode="emulate", inputs=kept)
+        fs_o = np.zeros((P, P), dtype=np.int64)
+        hist, w_o, worst = [], None, np.inf
+        for s in range(1, S + 1):
+            st = own[s - 1]
+            if not st.anchor:
+                valid = fs_o > 0
+                E = oracle.predicted_errors(w_o, np.array(hist).reshape(-1, P), fs_o, valid, s)
+                m = decision_margins(offs, cfg.frame_tokens, pol, E, valid)
+                worst = min([worst] + m)
+            assert np.array_equal(st.mask, masks[s - 1]), f"step {s}: free-running oracle"
+            hist.append(st.delta if st.delta is not None else np.zeros(P))
+            if st.w is not None:
+                w_o = st.w.astype(np.float32)
+            fs_o[st.mask == FRESH] = s
+        log(f"free-running oracle: {S} steps equal; smallest decision margin {worst:.3e}")
+        assert worst >= FREE_RUN_MARGIN
 
     # measurements against the oracle replaying the same masks (same cache rounding)
     rep = oracle.run_planner(cfg, heads, pol, masks=masks, cache_mode="emulate", inputs=kept)

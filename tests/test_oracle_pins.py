@@ -334,9 +334,30 @@ def test_round_bf16_matches_torch_on_float32_values():
     assert oatt.round_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -40]))[0] == 1 + 2.0 ** -7
 
 
-def test_round_f32_matches_numpy_cast():
-    x = np.array([1 / 3, 2 / 3, 1e-3, -7.1234567891])
-    assert np.array_equal(oatt.round_f32(x), x.astype(np.float32).astype(np.float64))
+def test_round_f32_hand_worked_values():
+    """Round-to-nearest-even to float32 (24 significant bits) on values worked out by hand,
+    so that truncation, rounding half away from zero or half up, or a lost sign fail."""
+    u = 2.0 ** -23                     # float32 spacing in [1, 2)
+    cases = [
+        (1 + u / 2, 1.0),              # tie between 1 and 1 + u: the even one, 1
+        (1 + 3 * u / 2, 1 + 2 * u),    # tie between 1 + u and 1 + 2u: the even one, 1 + 2u
+        (1 + u / 2 + 2.0 ** -40, 1 + u),   # just above a tie: up
+        (1 + u / 2 - 2.0 ** -40, 1.0),     # just below a tie: down
+        (-(1 + 3 * u / 2), -(1 + 2 * u)),  # the same tie, negative
+        (2 - 2.0 ** -25, 2.0),         # above the midpoint 2 - 2^-24 of [2 - u, 2]: up to 2
+        (2 - 3 * 2.0 ** -25, 2 - u),   # below that midpoint: down to 2 - u
+        # 1/3 = 2^-25 * (2^25 / 3) and 2^25 / 3 = 11184810.67 has 24 significant bits
+        (1.0 / 3.0, 11184811 * 2.0 ** -25),
+        (1.5 * 2.0 ** -149, 2.0 ** -148),  # subnormal tie between 1 and 2 units: 2 (even)
+        (2.0 ** -150, 0.0),            # subnormal tie between 0 and 1 unit: 0 (even)
+        (1.0 + 2.0 ** -30, 1.0),
+        (-7.25, -7.25),                # exact values stay
+    ]
+    x = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases])
+    got = oatt.round_f32(x)
+    assert np.array_equal(got, want), list(zip(x, got, want))
+    assert np.signbit(oatt.round_f32(np.array([-(2.0 ** -150)])))[0]   # rounds to -0
 
 
 # ----------------------------------------------------------------------------------------
