@@ -39,7 +39,7 @@ from workloads.gen import head_steps_packed, head_steps  # noqa: E402
 METRIC = "dense-equiv attention TFLOP/s + ms/step, % of MFMA+HBM roofline, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
-def kernel_label(head_dim, planner, fp8):
+def kernel_label(head_dim, planner, fp8, fixed=True):
     """Name of the step kernel instantiation a run's steady steps launch: <padded head dim,
     planner measurement compiled in, fp8 cache, fixed reference>.  Steps after the anchor run
     the fixed-reference pass (followed by the running-maximum kernel as a conditional second
@@ -47,7 +47,7 @@ def kernel_label(head_dim, planner, fp8):
     running-maximum kernel."""
     dp = 64 if head_dim <= 64 else (96 if head_dim <= 96 else 128)
     t = lambda b: "true" if b else "false"
-    return f"step_bf16<{dp}, {t(planner)}, {t(fp8)}, true>"
+    return f"step_bf16<{dp}, {t(planner)}, {t(fp8)}, {t(fixed)}>"
 
 
 def _gen_job(args):
@@ -56,7 +56,8 @@ def _gen_job(args):
 
 
 def _oracle_job(args):
-    """fp64 oracle on one head for `steps` steps; returns its wall time (1 BLAS thread)."""
+    """fp64 oracle on one head for `steps` steps; returns (b, h, steps, wall time) with one
+    BLAS thread (inputs drawn before the clock starts)."""
     cfg, b, h, steps = args
     from threadpoolctl import threadpool_limits
     import oracle
@@ -64,7 +65,54 @@ def _oracle_job(args):
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         oracle.run_head(cfg, b, h, steps=steps, inputs=inputs)
-        return time.perf_counter() - t0
+        return b, h, steps, time.perf_counter() - t0
+
+
+def cpu_share():
+    """Host CPUs this process may run on (its affinity set), else os.cpu_count()."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(pool, procs, cfg, anchor_steps, steady_steps):
+    """The fp64 oracle as it stands, timed on the host: one process per core, one BLAS thread
+    each.  procs / 2 heads each run twice at once, as step 1 alone (the anchor) and as steps
+    1-2 (anchor + one steady step; every steady step of the schedule has the same blocks), so
+    a head's steady step is the difference of its two runs.  The per-step time of the whole
+    workload on `procs` cores weights anchor and steady steps as the GPU run did and spreads
+    the B*H heads over the cores (heads are independent)."""
+    nh = max(1, procs // 2)
+    heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)][:nh]
+    jobs = [(cfg, b, h, n) for (b, h) in heads for n in (1, 2)]
+    t1 = time.perf_counter()
+    res = pool.map(_oracle_job, jobs, chunksize=1)
+    wall = time.perf_counter() - t1
+    one = {(b, h): t for b, h, n, t in res if n == 1}
+    two = {(b, h): t for b, h, n, t in res if n == 2}
+    t_anchor = float(np.median(list(one.values())))
+    t_steady = float(np.median([two[k] - one[k] for k in heads]))
+    per_head = (anchor_steps * t_anchor + steady_steps * t_steady) / (anchor_steps + steady_steps)
+    ms_step = per_head * cfg.batch * cfg.heads / procs * 1e3
+    dense = 4.0 * cfg.batch * cfg.heads * cfg.tokens ** 2 * cfg.head_dim
+    return {
+        "value": round(dense / (ms_step * 1e-3) / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": procs,
+        "ms_per_step": round(ms_step, 1),
+        "anchor_step_s_per_head": round(t_anchor, 3),
+        "steady_step_s_per_head": round(t_steady, 3),
+        "host_logical_cpus": os.cpu_count(),
+        "cpu_share": cpu_share(),
+        "cpu_model": cpu_model(),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle (one process per core, 1 BLAS thread, {len(jobs)} "
+                  f"processes): heads {heads[0]}..{heads[-1]} of {cfg.batch}x{cfg.heads}, each "
+                  f"as step 1 alone and as steps 1-2; per-head step time weighted "
+                  f"{anchor_steps} anchor : {steady_steps} steady as in the timed GPU steps, "
+                  f"times {cfg.batch * cfg.heads} heads / {procs} cores (sample wall "
+                  f"{wall:.1f} s)"}
 
 
 def mask_work(M, reuse_ptr, n, bh, D, cache_elem=2):
@@ -93,9 +141,10 @@ def kernel_source_digest():
 
 
 def measured_traffic(digest, kernel, workload):
-    """HBM bytes per step of the step kernel (every dispatch of the step summed) from
-    committed rocprofv3 counter runs, only if they were taken on the current kernel source,
-    the same kernel instantiation and the same workload and step mix (else None)."""
+    """HBM bytes per launch of the dominant kernel (the fixed-reference pass of a steady step)
+    from committed rocprofv3 FETCH_SIZE and WRITE_SIZE runs, each scaled by what the counter
+    reads for a plain device copy of known size; only if they were taken on the current kernel
+    source, the same kernel instantiation and the same workload (else None)."""
     path = os.path.join(ROOT, "profiles", "step_bf16_traffic.json")
     try:
         with open(path) as f:
@@ -105,16 +154,17 @@ def measured_traffic(digest, kernel, workload):
     if t.get("kernel_source_digest") != digest or t.get("kernel") != kernel or \
             not str(t.get("workload", "")).startswith(workload):
         return None
-    return t.get("hbm_bytes_per_step")
+    return (t["fetch_size_kib_fixed_pass_mean"] * 1024 * t["fetch_scale"]
+            + t["write_size_kib_fixed_pass_mean"] * 1024 * t["write_scale"])
 
 
-def hbm_roofline(traffic, cache_bytes_per_step, kernel_ms_per_step):
-    """The step kernels' HBM rate against the 8 TB/s peak: the counted traffic (rocprofv3
-    FETCH_SIZE + WRITE_SIZE per step) when the stored counters match this kernel and
-    workload, else the algorithmic cache bytes (reused states read + fresh states written
-    back), each over the step kernels' time per step."""
-    sec = kernel_ms_per_step * 1e-3
-    cache_gbs = cache_bytes_per_step / sec / 1e9
+def hbm_roofline(traffic, cache_bytes, kernel_ms):
+    """The dominant kernel's HBM rate against the 8 TB/s peak: its counted traffic per launch
+    (rocprofv3 FETCH_SIZE + WRITE_SIZE) when the stored counters match this kernel and
+    workload, else its algorithmic cache bytes (reused states read + fresh states written
+    back), each over its measured duration."""
+    sec = kernel_ms * 1e-3
+    cache_gbs = cache_bytes / sec / 1e9
     counted = traffic / sec / 1e9 if traffic else None
     achieved = counted if counted is not None else cache_gbs
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -215,15 +265,21 @@ def main():
     ap.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
                     help="layout of Q, K, V and out: [B, H, N, D] or [B, N, H, D] (the inputs "
                          "are staged in that layout before the timed region)")
+    ap.add_argument("--out", choices=["f32", "bf16"], default="f32",
+                    help="output element type: f32 (the bench line) or bf16 (rounded from the "
+                         "f32 result in the epilogue)")
+    ap.add_argument("--compact", action="store_true",
+                    help="with --merge: after each run's merges, compact the cache onto one "
+                         "slot per stored state (and expand it back before the next anchor)")
     ap.add_argument("--offload", action="store_true",
                     help="after the timed steps, time one offload of the cache's state to "
                          "pinned host memory and its restore into a new device buffer "
                          "(reported as `offload`, outside the timed region)")
     ap.add_argument("--planner-group", type=int, default=1)
     ap.add_argument("--planner-anchor-period", type=int, default=0)
-    ap.add_argument("--cpu-heads", type=int, default=8)
-    ap.add_argument("--cpu-steps", type=int, default=3)
-    ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--workers", type=int, default=min(16, cpu_share()),
+                    help="host processes for the input generator and the CPU baseline (one "
+                         "per core; at most 16, the host share of one GPU)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (outside the timed "
                          "region) as the reference for hardware traffic counters")
@@ -265,13 +321,14 @@ def main():
     print(f"[bench] inputs staged in HBM: {S} steps x 3 x {B}x{H}x{N}x{D} {cfg.qkv_dtype} "
           f"({t_gen:.1f} s)", file=sys.stderr, flush=True)
 
-    geom = dita.geometry_from(cfg)
+    geom = dita.geometry_from(cfg, out_dtype=args.out)
     geom.layout = dita.LAYOUT_BNHD if args.layout == "bnhd" else dita.LAYOUT_BHND
     # blocks that can ever be non-skip: the anchor step's active set
     act = (dita.dita_policy_mask(geom, dita.policy_from(cfg.policy(1).as_anchor())) != 0)
     cache = dita.Cache(geom, active_mask=act.astype(np.uint8))
     out = torch.empty((B, N, H, D) if args.layout == "bnhd" else (B, H, N, D),
-                      dtype=torch.float32, device="cuda")
+                      dtype=torch.bfloat16 if args.out == "bf16" else torch.float32,
+                      device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     if args.policy == "planner":
         from workloads import Policy, PLANNER
@@ -309,9 +366,20 @@ def main():
     stream = torch.cuda.current_stream()
     step_masks = []
 
+    compact_bytes = []
+    if args.compact:
+        if not merge_sizes:
+            sys.exit("--compact applies with --merge")
+        spare = [torch.empty(cache.required_bytes, dtype=torch.uint8, device="cuda")]
+
     def run_step(k):
         s = k % S
         if s == 0:
+            if args.compact and cache.buffer.numel() < cache.required_bytes:
+                # back to the full slot table (into the spare buffer) before the anchor
+                old = cache.buffer
+                cache.expand(buffer=spare[0], stream=stream)
+                spare[0] = old
             cache.reset()
         cache.set_policy(policies[s])
         pl = cache.plan()                             # host copy of the plan, no device wait
@@ -321,6 +389,16 @@ def main():
         if s == 0:
             for g, sel in merge_sel:
                 cache.merge_groups(g, select=sel, stream=stream)
+            if args.compact:
+                # onto one slot per stored state, in a buffer held aside for it
+                need = cache.compact_bytes()
+                if spare[0].numel() < need or not compact_bytes:
+                    spare[0] = torch.empty(need, dtype=torch.uint8, device="cuda")
+                old = cache.buffer
+                cache.compact(buffer=spare[0][:need] if spare[0].numel() > need else spare[0],
+                              stream=stream)
+                spare[0] = old
+                compact_bytes.append(need)
 
     for k in range(args.warmup):
         run_step(k)
@@ -360,11 +438,42 @@ def main():
     cache_bytes = sum(w[1] + w[2] for w in work)
     kern_ms = st["step_kernel_ms"]
     prep_ms = st["prep_kernel_ms"]
-    # per step: the step kernel's dispatches (after the anchor: the fixed-reference pass and the
-    # conditional second pass, which exits at once) between the library's HIP events
     launches = st["profiled_steps"]
     avg_kernel_ms = kern_ms / max(launches, 1)
-    achieved = fresh_flops / launches / (avg_kernel_ms * 1e-3) / 1e12
+    # The dominant kernel: the fixed-reference pass, which every step after a reset's first
+    # runs (each of its fresh blocks has a state from an earlier step), timed by the library's
+    # HIP events around it on its launch stream (with the conditional second pass after it,
+    # which exits at once unless a reference was rejected).  The first step after a reset
+    # runs the running-maximum kernel alone; it is reported on its own.
+    fixed_steps = st["fixed_ref_steps"]
+    steady_work = [w for w, s in zip(work, kinds) if s != 0]
+    anchor_work = [w for w, s in zip(work, kinds) if s == 0]
+    bf16_path = cfg.qkv_dtype == "bf16"
+    if bf16_path and fixed_steps != len(steady_work):
+        sys.exit(f"bench: {fixed_steps} steps ran the fixed-reference pass, expected "
+                 f"{len(steady_work)} (the steps after each reset's first)")
+    if bf16_path and fixed_steps:
+        fixed_ms = st["fixed_ref_kernel_ms"] / fixed_steps
+        steady_flops = sum(w[0] for w in steady_work) / len(steady_work)
+        achieved = steady_flops / (fixed_ms * 1e-3) / 1e12
+        dom_ms, dom_flops = fixed_ms, steady_flops
+        dom_cache_bytes = sum(w[1] + w[2] for w in steady_work) / len(steady_work)
+    else:
+        achieved = fresh_flops / launches / (avg_kernel_ms * 1e-3) / 1e12
+        dom_ms, dom_flops = avg_kernel_ms, fresh_flops / launches
+        dom_cache_bytes = cache_bytes / K
+    anchor_launches = launches - fixed_steps
+    anchor_roof = None
+    if bf16_path and anchor_launches and anchor_work:
+        a_ms = (kern_ms - st["fixed_ref_kernel_ms"]) / anchor_launches
+        a_flops = sum(w[0] for w in anchor_work) / len(anchor_work)
+        a_ach = a_flops / (a_ms * 1e-3) / 1e12
+        anchor_roof = {"kernel": kernel_label(D, args.policy == "planner",
+                                              cfg.cache_dtype == "fp8", fixed=False),
+                       "steps": anchor_launches, "kernel_ms": round(a_ms, 4),
+                       "fresh_tflop": round(a_flops / 1e12, 4),
+                       "achieved": round(a_ach, 2), "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(a_ach / PEAK_BF16_TFLOPS, 4)}
     digest = kernel_source_digest()
     label = kernel_label(D, args.policy == "planner", cfg.cache_dtype == "fp8")
     # the counter run covers the fixed schedule without merging, on [B, H, N, D] inputs
@@ -392,16 +501,18 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "heads": H, "tokens": N, "head_dim": D,
                    "partitions": cfg.num_partitions, "denoise_steps": S,
                    "schedule": schedule_desc,
-                   "cache": f"{cfg.cache_dtype} O + f32 lse", "out": "f32",
+                   "cache": f"{cfg.cache_dtype} O + f32 lse", "out": args.out,
                    "layout": args.layout},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": label,
-                     "kernel_ms_per_step": round(avg_kernel_ms, 4),
-                     "fresh_tflop_per_step": round(fresh_flops / launches / 1e12, 4),
+                     "launches": fixed_steps if bf16_path else launches,
+                     "kernel_ms": round(dom_ms, 4),
+                     "fresh_tflop_per_launch": round(dom_flops / 1e12, 4),
                      "kernel_source_digest": digest},
-        "roofline_hbm": hbm_roofline(traffic, cache_bytes / K, avg_kernel_ms),
+        "roofline_anchor": anchor_roof,
+        "roofline_hbm": hbm_roofline(traffic, dom_cache_bytes, dom_ms),
         "roofline_combined": {
             "t_roof_ms_per_step": round(t_roof_sum * 1e3 / K, 4),
             "frac_sum_form": round(t_roof_sum / wall, 4),
@@ -410,33 +521,22 @@ def main():
         "breakdown": {
             "anchor_step_ms": round(float(np.median(anchor_ms)), 4) if anchor_ms else None,
             "steady_step_ms": round(float(np.median(steady_ms)), 4) if steady_ms else None,
+            "step_kernels_ms_per_step": round(avg_kernel_ms, 4),
             "prep_kernel_ms_per_step": round(prep_ms / max(launches, 1), 4),
             "device_fresh_blocks": st["device_fresh_blocks"],
             "host_fresh_blocks": st["host_fresh_blocks"]},
     }
 
+    if compact_bytes:
+        result["compaction"] = {"full_buffer_bytes": cache.required_bytes,
+                                "compacted_buffer_bytes": compact_bytes[-1],
+                                "ratio": round(compact_bytes[-1] / cache.required_bytes, 4)}
     if args.offload:
         result["offload"] = time_offload(dita, cache, stream)
 
     if not args.no_cpu_baseline:
-        heads = [(0, h) for h in range(min(args.cpu_heads, H))]
-        nsteps = min(args.cpu_steps, S)
-        t1 = time.perf_counter()
-        times = pool.map(_oracle_job, [(cfg, b, h, nsteps) for b, h in heads],
-                         chunksize=1)
-        cpu_wall = max(times)
-        sample_flops = 4.0 * N * N * D * len(heads) * nsteps
-        result["cpu_baseline"] = {
-            "value": round(sample_flops / cpu_wall / 1e12, 6),
-            "unit": "TFLOP/s",
-            "cores": min(len(heads), args.workers),
-            "cpu_model": cpu_model(),
-            "kind": "oracle",
-            "sample": f"fp64 numpy oracle, heads {heads[0][1]}..{heads[-1][1]} of {H} "
-                      f"(one process each, 1 BLAS thread), steps 1..{nsteps} of the same "
-                      f"workload (anchor + {nsteps - 1} reuse steps); dense-equivalent "
-                      f"FLOPs of the sample / slowest head's wall time "
-                      f"({cpu_wall:.1f} s; pool wall {time.perf_counter() - t1:.1f} s)"}
+        result["cpu_baseline"] = cpu_baseline(pool, args.workers, cfg, len(anchor_ms),
+                                              len(steady_ms))
     pool.close()
     pool.join()
     print(json.dumps(result))

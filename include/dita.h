@@ -99,6 +99,11 @@ typedef struct dita_geometry {
   float softmax_scale;                      /* tau; <= 0 selects 1/sqrt(D)                  */
   int32_t layout;                           /* dita_layout of Q, K, V, out; zero-initialise
                                                the struct for BHND                          */
+  dita_dtype out_dtype;                     /* element type of out: F32 (0, the default of a
+                                               zero-initialised struct) or, with bf16
+                                               Q/K/V, BF16: the f32 result rounded to
+                                               nearest even, for a consumer that takes bf16
+                                               (half the bytes written)                     */
 } dita_geometry;
 
 /* One step's block policy (DiTango, "Anchor-Guided Selection Planner"): which blocks are
@@ -154,8 +159,9 @@ typedef struct dita_step_stats {
   double last_cache_write_bytes; /* sum over fresh blocks of n_i (D*s_c + 4), times B*H      */
   uint64_t device_v_range_errors;/* cumulative count of V elements with |v| > 65504: the bf16
                                     path multiplies P V in fp16, into which every bf16 value of
-                                    that range converts exactly; steps that saw such values are
-                                    not valid                                                 */
+                                    magnitude 2^-14 to 65504 converts exactly (smaller ones,
+                                    fp16 subnormals, keep an absolute error under 2^-25);
+                                    steps that saw larger values are not valid               */
   uint64_t profiled_steps;       /* steps timed since profiling was enabled                  */
   double step_kernel_ms;         /* summed duration of the main step kernel over those steps */
   double prep_kernel_ms;         /* summed duration of the V-transpose kernel (bf16 only)    */
@@ -168,6 +174,11 @@ typedef struct dita_step_stats {
                                     it was cached) the whole step is computed again with the
                                     running maximum.  Results are
                                     the same either way, within rounding.                     */
+  uint64_t fixed_ref_steps;      /* profiled bf16 steps that ran the fixed-reference pass      */
+  double fixed_ref_kernel_ms;    /* their part of step_kernel_ms: the fixed-reference pass and
+                                    the conditional second pass after it (which exits at once
+                                    unless a reference was rejected); step_kernel_ms minus
+                                    this is the running-maximum steps' time (anchor steps)    */
 } dita_step_stats;
 
 typedef struct dita_cache dita_cache;
@@ -235,15 +246,15 @@ dita_status dita_get_block_plan(const dita_cache* cache, uint8_t* mask, int32_t*
 /* Run one denoising step's attention on `hip_stream` (a hipStream_t; NULL = default).
  *   q, k, v   device, [B,H,N,D] (or [B,N,H,D] with layout BNHD) of qkv_dtype (bf16: |v| <=
  *             65504, see device_v_range_errors), 16-byte aligned
- *   out       device, f32 in the same layout: the merged output; 16-byte aligned, overlapping
- *             neither q, k, v nor the cache buffer
+ *   out       device, the geometry's out_dtype (f32 or bf16) in the same layout: the merged
+ *             output; 16-byte aligned, overlapping neither q, k, v nor the cache buffer
  *   lse_out   device, [B,H,N] f32 natural-log L, or NULL; 4-byte aligned
  * Fresh blocks are recomputed and written back to their slots; reused blocks are read from
  * theirs.  Stream-asynchronous: returns after enqueueing.  On success the pending policy is
  * consumed, written slots become valid and the step counter advances.
  * Errors: INVALID_ARGUMENT, NO_POLICY, DEVICE. */
 dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, const void* v,
-                           float* out, float* lse_out, void* hip_stream);
+                           void* out, float* lse_out, void* hip_stream);
 
 /* Copy one cache slot out in plain layout (for checks and export), on `hip_stream`:
  *   o_out    device, n_i x D f32 row-major: the cached O_ij rows of query partition i
@@ -272,6 +283,37 @@ dita_status dita_cache_read_slot(dita_cache* cache, int32_t b, int32_t h, int32_
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (B*H or max partition rows / 32 above 65535), DEVICE. */
 dita_status dita_cache_merge_groups(dita_cache* cache, int32_t group, const uint8_t* select,
                                     int32_t* merged, void* hip_stream);
+
+/* Compaction of merged groups (DiTango, "State-Centric Parallel Runtime / Composizione
+ * Dinamica dei Gruppi": merging stored states into coarser groups relieves memory pressure).
+ * After dita_cache_merge_groups the members of a merged group other than its first hold no
+ * state of their own; compaction moves the cache onto a slot table with one slot per stored
+ * state, so that the buffer it needs shrinks with the merges (a group of g states frees g - 1
+ * slots).
+ *
+ * dita_cache_compact_bytes: the bytes that table needs (host only; equals
+ *   dita_cache_required_bytes when nothing is merged).
+ *
+ * dita_cache_compact: bind device_buffer (device, 256-byte aligned, at least
+ *   dita_cache_compact_bytes, overlapping not the current buffer) and enqueue on hip_stream
+ *   the copy of the counters and every stored state into it.  Between steps only (no policy
+ *   pending).  The old buffer is the caller's again once hip_stream has passed the copy.
+ *   Steps then run as before -- a REUSE of a merged group reads its one state -- with one
+ *   restriction: a compacted group cannot be recomputed (a policy making any of its members
+ *   FRESH fails with POLICY), since its members have no slots; dita_cache_reset keeps the
+ *   groups (their states become invalid).  Merging further and compacting again is allowed.
+ *
+ * dita_cache_expand: the reverse: bind device_buffer (at least dita_cache_required_bytes)
+ *   with every active block's slot back and copy the stored states into it; merged groups
+ *   stay merged (their state in the first member's slot) and may be recomputed again.
+ * Errors: INVALID_ARGUMENT (NULL, misaligned, overlapping, other device, policy pending, expand
+ * of a cache that is not compacted), BUFFER_TOO_SMALL, OFFLOADED, UNSUPPORTED (B*H above
+ * 65535), DEVICE. */
+dita_status dita_cache_compact_bytes(const dita_cache* cache, size_t* bytes);
+dita_status dita_cache_compact(dita_cache* cache, void* device_buffer, size_t buffer_bytes,
+                               void* hip_stream);
+dita_status dita_cache_expand(dita_cache* cache, void* device_buffer, size_t buffer_bytes,
+                              void* hip_stream);
 
 /* Enable (1) or disable (0) kernel timing: the library records HIP events on the launch
  * stream around each of its kernels and sums their durations into dita_step_stats.

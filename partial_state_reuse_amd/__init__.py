@@ -40,7 +40,9 @@ EXPORTED = ["dita_version", "dita_last_error", "dita_policy_mask", "dita_partiti
             "dita_cache_free", "dita_set_block_policy", "dita_get_block_plan",
             "dita_attn_step", "dita_cache_read_slot", "dita_set_profiling", "dita_get_stats",
             "dita_planner_mask", "dita_get_planner_state", "dita_cache_merge_groups",
-            "dita_cache_offload_bytes", "dita_cache_offload", "dita_cache_restore"]
+            "dita_cache_offload_bytes", "dita_cache_offload", "dita_cache_restore",
+            "dita_cache_compact_bytes", "dita_cache_compact",
+            "dita_cache_expand"]
 
 
 class DitaError(RuntimeError):
@@ -57,7 +59,8 @@ class Geometry(ctypes.Structure):
                 ("grid_w", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("partition_offsets", ctypes.POINTER(ctypes.c_int32)),
                 ("qkv_dtype", ctypes.c_int32), ("cache_o_dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("layout", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("layout", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
 
 
 class BlockPolicy(ctypes.Structure):
@@ -77,7 +80,8 @@ class StepStats(ctypes.Structure):
                 ("last_cache_write_bytes", ctypes.c_double),
                 ("device_v_range_errors", ctypes.c_uint64),
                 ("profiled_steps", ctypes.c_uint64), ("step_kernel_ms", ctypes.c_double),
-                ("prep_kernel_ms", ctypes.c_double), ("device_ref_recomputes", ctypes.c_uint64)]
+                ("prep_kernel_ms", ctypes.c_double), ("device_ref_recomputes", ctypes.c_uint64),
+                ("fixed_ref_steps", ctypes.c_uint64), ("fixed_ref_kernel_ms", ctypes.c_double)]
 
 
 _P = ctypes.c_void_p
@@ -111,6 +115,9 @@ _sig = {
     "dita_cache_offload_bytes": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
     "dita_cache_offload": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     "dita_cache_restore": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P]),
+    "dita_cache_compact_bytes": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
+    "dita_cache_compact": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    "dita_cache_expand": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -134,10 +141,11 @@ def _u8(arr):
 
 def make_geometry(batch, heads, tokens, head_dim, frames, grid_h, grid_w, num_partitions,
                   dtype="bf16", offsets=None, softmax_scale=0.0, cache_dtype=None,
-                  layout="bhnd"):
+                  layout="bhnd", out_dtype="f32"):
     """A Geometry; `offsets` (P+1 ints) or None for the array_split rule; `cache_dtype`
     (cached O) defaults to `dtype` ("fp8" = e4m3, with bf16 Q/K/V); `layout` of Q, K, V and
-    out: "bhnd" ([B, H, N, D]) or "bnhd" ([B, N, H, D])."""
+    out: "bhnd" ([B, H, N, D]) or "bnhd" ([B, N, H, D]); `out_dtype` "f32" or "bf16" (with
+    bf16 Q/K/V)."""
     g = Geometry()
     g.batch, g.heads, g.tokens, g.head_dim = batch, heads, tokens, head_dim
     g.frames, g.grid_h, g.grid_w, g.num_partitions = frames, grid_h, grid_w, num_partitions
@@ -148,6 +156,7 @@ def make_geometry(batch, heads, tokens, head_dim, frames, grid_h, grid_w, num_pa
     g.cache_o_dtype = cd
     g.softmax_scale = softmax_scale
     g.layout = _LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    g.out_dtype = _DTYPES[out_dtype] if isinstance(out_dtype, str) else int(out_dtype)
     if offsets is not None:
         arr = (ctypes.c_int32 * len(offsets))(*[int(x) for x in offsets])
         g._offsets_keepalive = arr
@@ -285,7 +294,10 @@ class Cache:
 
     def step(self, q, k, v, out=None, lse=None, want_lse=True, stream=None):
         """Enqueue one step on `stream` (default: torch's current stream).  q/k/v are
-        contiguous [B,H,N,D] device tensors; returns (out [B,H,N,D] f32, lse [B,H,N] f32)."""
+        contiguous [B,H,N,D] (or [B,N,H,D]) device tensors; returns (out in the same layout,
+        of the geometry's out dtype (f32 or bf16), lse [B,H,N] f32).  Caller-supplied `out` /
+        `lse` must be of those dtypes, contiguous, of those shapes and on q's device; anything
+        else raises ValueError before a launch."""
         import torch
         for t in (q, k, v):
             if not t.is_contiguous():
@@ -299,15 +311,31 @@ class Cache:
         want = torch.bfloat16 if g.qkv_dtype == BF16 else torch.float32
         if q.dtype != want or k.dtype != want or v.dtype != want:
             raise ValueError(f"q, k, v must be {want}")
+        lse_shape = (g.batch, g.heads, g.tokens)
+        out_dt = torch.bfloat16 if g.out_dtype == BF16 else torch.float32
+        for name, t, shp, dt in (("out", out, shape, out_dt), ("lse", lse, lse_shape,
+                                                                torch.float32)):
+            if t is None:
+                continue
+            if t.dtype != dt:
+                raise ValueError(f"{name} must be {dt}, not {t.dtype}")
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} must have shape {shp}, not {tuple(t.shape)}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if t.device != q.device:
+                raise ValueError(f"{name} must be on {q.device}, not {t.device}")
+        if k.device != q.device or v.device != q.device:
+            raise ValueError("q, k and v must be on one device")
+        if q.device.type != "cuda":
+            raise ValueError(f"q, k, v must be HIP device tensors, not on {q.device}")
         if out is None:
-            out = torch.empty(shape, dtype=torch.float32, device=q.device)
+            out = torch.empty(shape, dtype=out_dt, device=q.device)
         if lse is None and want_lse:
-            lse = torch.empty((g.batch, g.heads, g.tokens), dtype=torch.float32,
-                              device=q.device)
-        _check(_lib.dita_attn_step(self._h, _P(q.data_ptr()), _P(k.data_ptr()),
-                                   _P(v.data_ptr()), _P(out.data_ptr()),
-                                   _P(lse.data_ptr()) if lse is not None else None,
-                                   _P(_stream_handle(stream))))
+            lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+        _check(_lib.dita_attn_step(self._h, _P(q.data_ptr()), _P(k.data_ptr()), _P(v.data_ptr()),
+                  _P(out.data_ptr()), _P(lse.data_ptr()) if lse is not None else None,
+                  _P(_stream_handle(stream))))
         return out, lse
 
     def step_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr=None, stream_handle=None):
@@ -379,6 +407,44 @@ class Cache:
         torch.cuda.synchronize()
         self._host_state = None
 
+    def compact_bytes(self) -> int:
+        """Device bytes the cache needs with its merged groups compacted (one slot per stored
+        state)."""
+        n = ctypes.c_size_t(0)
+        _check(_lib.dita_cache_compact_bytes(self._h, ctypes.byref(n)))
+        return n.value
+
+    def _rebind(self, fn, nbytes, buffer, device, stream):
+        import torch
+        if buffer is None:
+            dev = device or (self.buffer.device if self.buffer is not None else "cuda")
+            buffer = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _check(fn(self._h, _P(buffer.data_ptr()),
+                  ctypes.c_size_t(buffer.numel() * buffer.element_size()),
+                  _P(_stream_handle(stream))))
+        self._old_buffer = self.buffer        # alive until the stream has passed the copy
+        self.buffer = buffer
+        return buffer
+
+    def compact(self, buffer=None, device=None, stream=None):
+        """Move the cache onto its compacted slot table in `buffer` (a uint8 device tensor of
+        at least compact_bytes(); None: a new one).  The old buffer is released after the
+        next synchronisation of this object (release_old_buffer)."""
+        return self._rebind(_lib.dita_cache_compact, self.compact_bytes(), buffer, device,
+                            stream)
+
+    def expand(self, buffer=None, device=None, stream=None):
+        """Move a compacted cache back onto the full slot table (required_bytes)."""
+        return self._rebind(_lib.dita_cache_expand, self.required_bytes, buffer, device,
+                            stream)
+
+    def release_old_buffer(self):
+        """Drop the buffer a compact / expand moved away from (synchronises the device)."""
+        import torch
+        if getattr(self, "_old_buffer", None) is not None:
+            torch.cuda.synchronize()
+            self._old_buffer = None
+
     def planner_state(self) -> dict:
         """The planner's measured state (waits for the last step's measurements)."""
         P = self.geom.num_partitions
@@ -407,7 +473,9 @@ class Cache:
                 "device_v_range_errors": s.device_v_range_errors,
                 "profiled_steps": s.profiled_steps, "step_kernel_ms": s.step_kernel_ms,
                 "prep_kernel_ms": s.prep_kernel_ms,
-                "device_ref_recomputes": s.device_ref_recomputes}
+                "device_ref_recomputes": s.device_ref_recomputes,
+                "fixed_ref_steps": s.fixed_ref_steps,
+                "fixed_ref_kernel_ms": s.fixed_ref_kernel_ms}
 
 
 def policy_from(p) -> BlockPolicy:
@@ -421,8 +489,9 @@ def policy_from(p) -> BlockPolicy:
                        max_error=getattr(p, "max_error", 0.0))
 
 
-def geometry_from(cfg, offsets=None) -> Geometry:
+def geometry_from(cfg, offsets=None, out_dtype="f32", layout="bhnd") -> Geometry:
     """Geometry from any object with the fields of workloads.Config."""
     return make_geometry(cfg.batch, cfg.heads, cfg.tokens, cfg.head_dim, cfg.frames,
                          cfg.grid_h, cfg.grid_w, cfg.num_partitions, cfg.qkv_dtype,
-                         offsets=offsets, cache_dtype=getattr(cfg, "cache_dtype", None))
+                         offsets=offsets, cache_dtype=getattr(cfg, "cache_dtype", None),
+                         layout=layout, out_dtype=out_dtype)

@@ -48,6 +48,7 @@ struct Geo {
   int frames = 0, gh = 0, gw = 0, F = 0;
   dita_dtype qkv = DITA_BF16, cache_o = DITA_BF16;
   int layout = DITA_LAYOUT_BHND;
+  dita_dtype out = DITA_F32;
   float tau = 0.f;
   std::vector<int32_t> offs;    // P+1
   std::vector<int64_t> c2;      // doubled centroids
@@ -93,6 +94,11 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
   if (g->layout != DITA_LAYOUT_BHND && g->layout != DITA_LAYOUT_BNHD)
     return fail(DITA_ERR_INVALID_ARGUMENT, "unknown layout %d", g->layout);
   r.layout = g->layout;
+  if (g->out_dtype != DITA_F32 && g->out_dtype != DITA_BF16)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "out_dtype must be F32 or BF16");
+  if (g->out_dtype == DITA_BF16 && g->qkv_dtype != DITA_BF16)
+    return fail(DITA_ERR_UNSUPPORTED, "a bf16 output needs bf16 Q/K/V");
+  r.out = g->out_dtype;
   if ((int64_t)r.H * r.D > INT32_MAX) return fail(DITA_ERR_SHAPE, "heads x head_dim too large");
   if (r.bf16()) {
     r.DP = dita::bf16_padded_dim(r.D);
@@ -434,6 +440,7 @@ struct TimedStep {
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
   bool pending = false;
   bool two_kernels = false;
+  bool fixed_ref = false;            // the step ran the fixed-reference pass
 };
 constexpr int kTimingRing = 64;
 
@@ -468,6 +475,7 @@ struct dita_cache {
   double last_flops = 0, last_rd = 0, last_wr = 0;
   // device state, created at the first step
   bool dev_init = false;
+  bool counters_init = false;        // device counters cleared (first step of either kind)
   int device = -1;
   int32_t* staging = nullptr;        // pinned host, kPlanSlots * plan_bytes
   PlanSlot pslots[dita::kPlanSlots];
@@ -478,6 +486,8 @@ struct dita_cache {
   int timing_next = 0;
   uint64_t profiled_steps = 0;
   double step_ms = 0, prep_ms = 0;
+  uint64_t fixed_steps = 0;          // profiled steps that ran the fixed-reference pass
+  double fixed_ms = 0;               // their step-kernel time
   // planner state since the last reset
   int32_t steps_since_reset = 0;
   std::vector<int32_t> fresh_step;   // P*P step since reset of the last FRESH (0 = never)
@@ -487,6 +497,12 @@ struct dita_cache {
   // group composition: head[i*P+j] = the block whose slot holds the state covering (i, j)
   // (j itself unless (i, j) was merged into a group headed by another block)
   std::vector<int32_t> head;
+  // compaction: the slot table of the active set as allocated, and whether the cache now
+  // runs on a compacted table (merged members share their group's slot)
+  std::vector<int32_t> full_slot_of;
+  int full_num_slots = 0;
+  bool compacted = false;
+  std::vector<int32_t> remap_host;   // {new slot, old slot} pairs of the last rebind
   int32_t* merge_host = nullptr;     // pinned staging of the merge jobs (L.merge_bytes)
   hipEvent_t merge_event = nullptr;
   bool merge_event_recorded = false;
@@ -587,6 +603,7 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->cache_fp8 = g.cache_o == DITA_FP8_E4M3 ? 1 : 0;
   a->fixed_ref = 0;
   a->fixup = 0;
+  a->out_bf16 = g.out == DITA_BF16 ? 1 : 0;
   a->diag_snap = nullptr;
 }
 
@@ -609,10 +626,13 @@ dita_status device_init(dita_cache* c, hipStream_t s) {
     st = hip_check(hipEventCreateWithFlags(&ps.event, hipEventDisableTiming), "hipEventCreate");
     if (st) return st;
   }
-  st = hip_check(dita::launch_zero_counters(
-                     (unsigned long long*)(c->dev + c->L.counters), 32, s),
-                 "counter clear launch");
-  if (st) return st;
+  if (!c->counters_init) {
+    st = hip_check(dita::launch_zero_counters(
+                       (unsigned long long*)(c->dev + c->L.counters), 32, s),
+                   "counter clear launch");
+    if (st) return st;
+    c->counters_init = true;
+  }
   c->device = dev;
   c->dev_init = true;
   return ok();
@@ -628,11 +648,12 @@ dita_status drain_timing(dita_cache* c, TimedStep& t) {
   if (st) return st;
   st = hip_check(hipEventElapsedTime(&b, t.ev[1], t.ev[2]), "hipEventElapsedTime");
   if (st) return st;
-  if (t.two_kernels) {
-    c->prep_ms += a;
-    c->step_ms += b;
-  } else {
-    c->step_ms += a + b;
+  const double step = t.two_kernels ? b : a + b;
+  if (t.two_kernels) c->prep_ms += a;
+  c->step_ms += step;
+  if (t.fixed_ref) {
+    c->fixed_ms += step;
+    ++c->fixed_steps;
   }
   ++c->profiled_steps;
   t.pending = false;
@@ -794,6 +815,8 @@ dita_status dita_cache_alloc(const dita_geometry* geom, const uint8_t* active_ma
   c->w.assign((size_t)c->g.P * c->g.P, 0.f);
   c->head.resize((size_t)c->g.P * c->g.P);
   for (size_t b = 0; b < c->head.size(); ++b) c->head[b] = (int32_t)(b % c->g.P);
+  c->full_slot_of = c->slot_of;
+  c->full_num_slots = ns;
   *out = c;
   return ok();
 }
@@ -809,7 +832,10 @@ dita_status dita_cache_reset(dita_cache* c) {
   c->have_w = false;
   c->delta_hist.clear();
   if (c->meas_pending) c->meas_discard = true;   // its copy may still be in flight
-  for (size_t b = 0; b < c->head.size(); ++b) c->head[b] = (int32_t)(b % c->g.P);
+  // merged groups dissolve, except on a compacted table, whose members share a slot until
+  // dita_cache_expand
+  if (!c->compacted)
+    for (size_t b = 0; b < c->head.size(); ++b) c->head[b] = (int32_t)(b % c->g.P);
   return ok();
 }
 
@@ -889,6 +915,11 @@ dita_status dita_set_block_policy(dita_cache* c, const dita_block_policy* policy
         return fail(DITA_ERR_POLICY, "block (%d,%d) is merged with (%d,%d): a merged group is "
                     "reused or recomputed as a whole", i, j, i, c->head[b]);
     }
+  if (c->compacted)
+    for (size_t b = 0; b < M.size(); ++b)
+      if (covered[b] && M[b] == DITA_FRESH)
+        return fail(DITA_ERR_POLICY, "block (%d,%d) is compacted with its group into one slot; "
+                    "recomputing it needs dita_cache_expand first", (int)(b / P), (int)(b % P));
   build_lists(c->g.P, M, covered.data(), c->valid.data(), &c->pending);
   c->pending.planner_w = meas_w;
   c->pending.planner_delta = meas_delta;
@@ -912,7 +943,7 @@ dita_status dita_get_block_plan(const dita_cache* c, uint8_t* mask, int32_t* fre
 }
 
 dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const void* v,
-                           float* out, float* lse_out, void* hip_stream) {
+                           void* out, float* lse_out, void* hip_stream) {
   if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
   if (!q || !k || !v || !out) return fail(DITA_ERR_INVALID_ARGUMENT, "q, k, v, out required");
   for (const void* p : {q, k, v, (const void*)out})
@@ -1002,6 +1033,7 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
     if (st) return st;
     ts->pending = true;
     ts->two_kernels = c->g.bf16();
+    ts->fixed_ref = c->g.bf16() && a.fixed_ref && (!a.delta_part || a.diag_snap);
     c->timing_next = (c->timing_next + 1) % kTimingRing;
   }
   if (measure) {
@@ -1082,6 +1114,8 @@ dita_status dita_set_profiling(dita_cache* c, int32_t enable) {
     if (st) return st;
     c->profiled_steps = 0;
     c->step_ms = c->prep_ms = 0;
+    c->fixed_steps = 0;
+    c->fixed_ms = 0;
   }
   c->profiling = enable != 0;
   return ok();
@@ -1247,7 +1281,7 @@ dita_status dita_cache_restore(dita_cache* c, void* device_buffer, size_t buffer
   if (host_bytes < need)
     return fail(DITA_ERR_INVALID_ARGUMENT, "host_src holds %zu bytes, %zu needed", host_bytes,
                 need);
-  if (c->dev_init) {
+  if (c->device >= 0) {
     int dev = -1;
     dita_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
     if (st) return st;
@@ -1274,6 +1308,134 @@ dita_status dita_cache_restore(dita_cache* c, void* device_buffer, size_t buffer
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Move the cache onto another slot table in a new device buffer: the counters, and for each
+// {new slot, old slot} pair the stored state, copied device to device on the stream.
+dita_status rebind_slots(dita_cache* c, std::vector<int32_t> new_slot_of, int new_slots,
+                         const std::vector<int32_t>& pairs, void* device_buffer,
+                         size_t buffer_bytes, void* hip_stream, bool compacted) {
+  if (!device_buffer) return fail(DITA_ERR_INVALID_ARGUMENT, "device_buffer is NULL");
+  if ((uintptr_t)device_buffer % 256 != 0)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "device_buffer must be 256-byte aligned");
+  const Layout NL = compute_layout(c->g, new_slots);
+  if (buffer_bytes < NL.total)
+    return fail(DITA_ERR_BUFFER_TOO_SMALL, "buffer holds %zu bytes, %zu needed", buffer_bytes,
+                NL.total);
+  if ((uint8_t*)device_buffer < c->dev + c->dev_bytes &&
+      c->dev < (uint8_t*)device_buffer + buffer_bytes)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "the new buffer overlaps the cache's buffer");
+  if ((int64_t)c->g.B * c->g.H > 65535)
+    return fail(DITA_ERR_UNSUPPORTED, "compaction supports B*H up to 65535");
+  if (c->device >= 0) {
+    int dev = -1;
+    dita_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (st) return st;
+    if (dev != c->device)
+      return fail(DITA_ERR_INVALID_ARGUMENT, "rebind on device %d, the cache ran on device %d",
+                  dev, c->device);
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  uint8_t* nd = (uint8_t*)device_buffer;
+  dita_status st = hip_check(hipMemcpyAsync(nd + NL.counters, c->dev + c->L.counters,
+                                            offload_counter_bytes(c->L),
+                                            hipMemcpyDeviceToDevice, s), "counter copy");
+  if (st) return st;
+  const int npairs = (int)(pairs.size() / 2);
+  if (npairs > 0) {
+    // the pairs go through the new buffer's work-list area, rebuilt by the next step
+    c->remap_host = pairs;
+    int32_t* map = (int32_t*)(nd + NL.plans);
+    st = hip_check(hipMemcpyAsync(map, c->remap_host.data(), pairs.size() * 4,
+                                  hipMemcpyHostToDevice, s), "slot map upload");
+    if (st) return st;
+    st = hip_check(dita::launch_remap_slots(
+                       (const float*)(c->dev + c->L.lse), c->dev + c->L.o,
+                       (float*)(nd + NL.lse), nd + NL.o, map, npairs, c->g.B * c->g.H,
+                       c->num_slots, new_slots, c->g.slot_rows,
+                       (size_t)c->g.slot_rows * c->g.DP * c->g.cache_esz(), s),
+                   "remap_slots launch");
+    if (st) return st;
+  }
+  c->slot_of = std::move(new_slot_of);
+  c->num_slots = new_slots;
+  c->L = NL;
+  c->dev = nd;
+  c->dev_bytes = buffer_bytes;
+  c->compacted = compacted;
+  for (auto& ps : c->pslots) ps.used = false;   // work lists held the old slot numbers
+  return ok();
+}
+
+dita_status rebind_checks(const dita_cache* c) {
+  if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (c->offloaded) return fail(DITA_ERR_OFFLOADED, "the cache is offloaded; restore it first");
+  if (c->has_pending)
+    return fail(DITA_ERR_INVALID_ARGUMENT, "rebind between steps, before the next policy is set");
+  return ok();
+}
+
+// Slots of the compacted table: the active blocks that hold their own state (each merged
+// group once, at its head), in row-major order.
+int compact_slots(const dita_cache* c, std::vector<int32_t>* new_slot_of,
+                  std::vector<int32_t>* pairs) {
+  const int P = c->g.P;
+  if (new_slot_of) new_slot_of->assign((size_t)P * P, -1);
+  int n = 0;
+  for (size_t b = 0; b < (size_t)P * P; ++b) {
+    if (c->full_slot_of[b] < 0 || c->head[b] != (int32_t)(b % P)) continue;
+    if (new_slot_of) (*new_slot_of)[b] = n;
+    if (pairs && c->valid[b]) {
+      pairs->push_back(n);
+      pairs->push_back(c->slot_of[b]);
+    }
+    ++n;
+  }
+  if (new_slot_of)
+    for (size_t b = 0; b < (size_t)P * P; ++b)
+      if (c->full_slot_of[b] >= 0 && c->head[b] != (int32_t)(b % P))
+        (*new_slot_of)[b] = (*new_slot_of)[(b / P) * P + c->head[b]];
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+dita_status dita_cache_compact_bytes(const dita_cache* c, size_t* bytes) {
+  if (!c || !bytes) return fail(DITA_ERR_INVALID_ARGUMENT, "cache and bytes required");
+  *bytes = compute_layout(c->g, compact_slots(c, nullptr, nullptr)).total;
+  return ok();
+}
+
+dita_status dita_cache_compact(dita_cache* c, void* device_buffer, size_t buffer_bytes,
+                               void* hip_stream) {
+  dita_status st = rebind_checks(c);
+  if (st) return st;
+  std::vector<int32_t> slot_of, pairs;
+  const int n = compact_slots(c, &slot_of, &pairs);
+  return rebind_slots(c, std::move(slot_of), n, pairs, device_buffer, buffer_bytes, hip_stream,
+                      true);
+}
+
+dita_status dita_cache_expand(dita_cache* c, void* device_buffer, size_t buffer_bytes,
+                              void* hip_stream) {
+  dita_status st = rebind_checks(c);
+  if (st) return st;
+  if (!c->compacted) return fail(DITA_ERR_INVALID_ARGUMENT, "the cache is not compacted");
+  const int P = c->g.P;
+  std::vector<int32_t> pairs;
+  for (size_t b = 0; b < (size_t)P * P; ++b)
+    if (c->full_slot_of[b] >= 0 && c->head[b] == (int32_t)(b % P) && c->valid[b]) {
+      pairs.push_back(c->full_slot_of[b]);
+      pairs.push_back(c->slot_of[b]);
+    }
+  return rebind_slots(c, c->full_slot_of, c->full_num_slots, pairs, device_buffer, buffer_bytes,
+                      hip_stream, false);
+}
+
 dita_status dita_get_stats(const dita_cache* cc, dita_step_stats* s) {
   if (!cc || !s) return fail(DITA_ERR_INVALID_ARGUMENT, "cache and stats required");
   dita_cache* c = const_cast<dita_cache*>(cc);   // draining timing events updates sums only
@@ -1291,7 +1453,9 @@ dita_status dita_get_stats(const dita_cache* cc, dita_step_stats* s) {
   s->profiled_steps = c->profiled_steps;
   s->step_kernel_ms = c->step_ms;
   s->prep_kernel_ms = c->prep_ms;
-  if (c->dev_init) {
+  s->fixed_ref_steps = c->fixed_steps;
+  s->fixed_ref_kernel_ms = c->fixed_ms;
+  if (c->counters_init) {
     unsigned long long cnt[4] = {0, 0, 0, 0};
     dita_status st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
     if (st) return st;

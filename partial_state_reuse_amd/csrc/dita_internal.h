@@ -50,7 +50,7 @@ struct StepArgs {
   const void* q;
   const void* k;
   const void* v;
-  float* out;
+  void* out;                 // f32, or bf16 with out_bf16
   float* lse_out;            // may be null
   void* vt;                  // fp16 transposed-V scratch [B*H][DP][kt_pad]
   void* cache_o;             // bf16 / fp8: [B*H][slots][slot_rows/32][DP/32][64][16] elements
@@ -88,6 +88,7 @@ struct StepArgs {
   // pass (fixup = 1), which exits at once unless the first pass rejected a reference
   int32_t fixed_ref;
   int32_t fixup;
+  int32_t out_bf16;          // bf16 path: out in bf16 (round to nearest even) instead of f32
 };
 
 hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s);
@@ -113,5 +114,14 @@ hipError_t launch_merge_slots(const StepArgs& a, const int32_t* jobs, const int3
                               int njobs, int cache_esz, hipStream_t s);
 hipError_t launch_read_slot(const StepArgs& a, int bh, int slot, int i, float* o_out,
                             float* lse_out, int cache_esz, hipStream_t s);
+
+// Cache compaction / expansion: for each of the npairs {new slot, old slot} pairs of `map`
+// (device, 2 * npairs int32) and each of the bhs (b, h) pairs, copy the slot's lse row and O
+// from the old slot table's buffers to the new one's.  Grid (npairs, bhs); npairs and bhs up
+// to 2^31 - 1 and 65535.
+hipError_t launch_remap_slots(const float* old_lse, const void* old_o, float* new_lse,
+                              void* new_o, const int32_t* map, int npairs, int bhs,
+                              int old_slots, int new_slots, int slot_rows,
+                              size_t o_slot_bytes, hipStream_t s);
 
 }  // namespace dita

@@ -386,7 +386,7 @@ __device__ __forceinline__ void finish_rows(const StepArgs& a, int bh, int o_i, 
   const size_t bhN = (size_t)bh * a.N;
   if (myrow < n_i) {
     const float inv = 1.0f / l_row;
-    float* orow = a.out + head_base(a, bh) + (size_t)(o_i + myrow) * a.ld;
+    const size_t orow = head_base(a, bh) + (size_t)(o_i + myrow) * a.ld;   // element offset
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -395,7 +395,17 @@ __device__ __forceinline__ void finish_rows(const StepArgs& a, int bh, int o_i, 
         if (d < a.D) {
           f32x4 v = {acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
                      acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv};
-          *(f32x4*)(orow + d) = v;
+          if (a.out_bf16) {                       // uniform: 4 values rounded to bf16, 8 bytes
+            uint16_t e[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) e[t] = __builtin_bit_cast(uint16_t, (__bf16)v[t]);
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 w = {(uint32_t)e[0] | ((uint32_t)e[1] << 16),
+                             (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
+            *(u32x2*)((uint16_t*)a.out + orow + d) = w;
+          } else {
+            *(f32x4*)((float*)a.out + orow + d) = v;
+          }
         }
       }
     }
@@ -898,7 +908,7 @@ __global__ __launch_bounds__(64) void step_f32(StepArgs a) {
     m_row = mn;
   }
   if (ok) {
-    float* orow = a.out + hb + (size_t)(o_i + r) * ld;
+    float* orow = (float*)a.out + hb + (size_t)(o_i + r) * ld;
 #pragma unroll
     for (int d = 0; d < DP; ++d)
       if (d < D) orow[d] = acc[d] / l_row;
@@ -1205,7 +1215,38 @@ __global__ __launch_bounds__(256) void merge_slots(StepArgs a, const int32_t* jo
     a.cache_lse[((size_t)bh * a.num_slots + dst) * a.slot_rows + u * 32 + tid] = Ls[tid];
 }
 
+// ------------------------------------------------------------------------------------------
+// cache compaction / expansion: copy stored states between two slot tables
+// workgroup (k, bh): pair k = {new slot, old slot} of map; the slot's lse row (slot_rows f32)
+// and its O (o_slot_bytes, a multiple of 16) go from the old buffer to the new one.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void remap_slots(const float* old_lse, const uint8_t* old_o,
+                                                   float* new_lse, uint8_t* new_o,
+                                                   const int32_t* map, int old_slots,
+                                                   int new_slots, int slot_rows,
+                                                   long long o_slot_bytes) {
+  const int k = blockIdx.x, bh = blockIdx.y;
+  const int ns = map[2 * k], os = map[2 * k + 1];
+  const float* ls = old_lse + ((size_t)bh * old_slots + os) * slot_rows;
+  float* ld = new_lse + ((size_t)bh * new_slots + ns) * slot_rows;
+  for (int r = threadIdx.x; r < slot_rows; r += 256) ld[r] = ls[r];
+  const u32x4* src = (const u32x4*)(old_o + ((size_t)bh * old_slots + os) * (size_t)o_slot_bytes);
+  u32x4* dst = (u32x4*)(new_o + ((size_t)bh * new_slots + ns) * (size_t)o_slot_bytes);
+  for (long long w = threadIdx.x; w < o_slot_bytes / 16; w += 256) dst[w] = src[w];
+}
+
 }  // namespace
+
+hipError_t launch_remap_slots(const float* old_lse, const void* old_o, float* new_lse,
+                              void* new_o, const int32_t* map, int npairs, int bhs,
+                              int old_slots, int new_slots, int slot_rows,
+                              size_t o_slot_bytes, hipStream_t s) {
+  if (npairs == 0) return hipSuccess;
+  hipLaunchKernelGGL(remap_slots, dim3(npairs, bhs), dim3(256), 0, s, old_lse,
+                     (const uint8_t*)old_o, new_lse, (uint8_t*)new_o, map, old_slots,
+                     new_slots, slot_rows, (long long)o_slot_bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s) {
   hipLaunchKernelGGL(zero_u64, dim3((n + 63) / 64), dim3(64), 0, s, counters, n);

@@ -103,11 +103,17 @@ def sample_rows(offs, per_part, rng):
     return np.array(sorted(rows), dtype=np.int64)
 
 
+# Longest block, in keys, held to the fp32 bar as stated: the small fp32 workload's blocks.
+F32_STATED_KEYS = 64
+
+
 def f32_bar(n_keys, vmax):
     """Max-abs bar of the f32 path for blocks of up to n_keys keys and values up to vmax:
-    1e-5 (the bar stated for the small fp32 workload, whose blocks have 64 keys), or, for
-    longer blocks, four standard deviations of the random walk of sequential fp32
-    accumulation, 4 sqrt(n) 2^-24 max|V|, whichever is larger."""
+    exactly 1e-5 (the bar stated for the small fp32 workload) for blocks of up to its 64 keys;
+    for longer blocks, four standard deviations of the random walk of sequential fp32
+    accumulation, 4 sqrt(n) 2^-24 max|V|, if that is larger."""
+    if n_keys <= F32_STATED_KEYS:
+        return F32_MAX_ABS
     return max(F32_MAX_ABS, 4.0 * np.sqrt(float(n_keys)) * 2.0 ** -24 * float(vmax))
 
 
@@ -126,6 +132,16 @@ def bf16_ulp(x):
     """Spacing of bfloat16 values (8 significant bits) at |x|."""
     ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def bf16_out_bars(want):
+    """Bars of a bf16 output against the fp64 reference `want`.  The kernel rounds its f32
+    result o to bf16 (nearest even), which moves it by at most half a bf16 ulp at |o|, so
+    |rne(o) - want| <= |o - want| + ulp(|o|) / 2, with |o| <= |want| + 2e-2 by the f32
+    output's own bar.  Elementwise: 2e-2 + ulp(|want| + 2e-2) / 2; mean: 2e-3 plus the mean of
+    those half ulps."""
+    half = bf16_ulp(np.abs(np.asarray(want, np.float64)) + BF16_MAX_ABS) / 2
+    return BF16_MAX_ABS + half, BF16_MEAN_ABS + float(half.mean())
 
 
 def compare_cached(got, want_rounded, want_exact, bf16, what, f32_max=F32_MAX_ABS):

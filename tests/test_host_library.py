@@ -287,6 +287,36 @@ def test_layout_field():
     assert e.value.name == "INVALID_ARGUMENT"
 
 
+def test_step_rejects_bad_output_tensors_before_launch():
+    """Caller-supplied out / lse of the wrong dtype, shape, layout or device, and inputs that
+    are not on a HIP device, raise ValueError in the binding before the library is called
+    (host tensors only here; the cache is bound to an address never dereferenced)."""
+    torch = pytest.importorskip("torch")
+    cfg = CONFIGS[1]
+    c, g = fake_cache(cfg)
+    c.set_policy(dita.policy_from(cfg.policy(1)))
+    B, H, N, D = cfg.batch, cfg.heads, cfg.tokens, cfg.head_dim
+    q = k = v = torch.zeros((B, H, N, D), dtype=torch.float32)
+    good_out = torch.zeros((B, H, N, D), dtype=torch.float32)
+    good_lse = torch.zeros((B, H, N), dtype=torch.float32)
+    bad = [
+        ("out", dict(out=good_out.to(torch.bfloat16)), "float32"),
+        ("out", dict(out=good_out[:, :, : N - 1]), "shape"),
+        ("out", dict(out=torch.zeros((B, N, H, D), dtype=torch.float32)), "shape"),
+        ("out", dict(out=torch.zeros((B, H, D, N), dtype=torch.float32).transpose(2, 3)),
+         "contiguous"),
+        ("lse", dict(lse=good_lse.to(torch.float64)), "float32"),
+        ("lse", dict(lse=torch.zeros((B, H, N + 1), dtype=torch.float32)), "shape"),
+    ]
+    for name, kw, word in bad:
+        with pytest.raises(ValueError, match=word):
+            c.step(q, k, v, **kw)
+    with pytest.raises(ValueError, match="HIP device"):     # right tensors, but host memory
+        c.step(q, k, v, out=good_out, lse=good_lse)
+    assert c.stats()["steps_done"] == 0
+    c.free()
+
+
 def test_header_is_c_and_matches_the_binding(tmp_path):
     """include/dita.h compiles as plain C99, and its structs have the sizes and field offsets
     the ctypes binding declares (a mismatch would pass wrong arguments silently)."""
