@@ -317,6 +317,24 @@ def test_step_rejects_bad_output_tensors_before_launch():
     c.free()
 
 
+def test_out_dtype_field():
+    """The output dtype: f32 (the zero default) or bf16 with bf16 Q/K/V; it changes neither
+    the buffer size nor the plan; bf16 with f32 inputs and unknown values are rejected."""
+    cfg = CONFIGS[3]
+    sizes = {dt: dita.dita_cache_required_bytes(dita.geometry_from(cfg, out_dtype=dt))
+             for dt in ("f32", "bf16")}
+    assert sizes["f32"] == sizes["bf16"]
+    assert dita.geometry_from(cfg).out_dtype == dita.F32
+    with pytest.raises(dita.DitaError) as e:
+        dita.dita_cache_required_bytes(dita.geometry_from(CONFIGS[1], out_dtype="bf16"))
+    assert e.value.name == "UNSUPPORTED"
+    g = dita.geometry_from(cfg)
+    g.out_dtype = 2
+    with pytest.raises(dita.DitaError) as e:
+        dita.dita_cache_required_bytes(g)
+    assert e.value.name == "INVALID_ARGUMENT"
+
+
 def test_header_is_c_and_matches_the_binding(tmp_path):
     """include/dita.h compiles as plain C99, and its structs have the sizes and field offsets
     the ctypes binding declares (a mismatch would pass wrong arguments silently)."""
