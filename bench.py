@@ -268,6 +268,9 @@ def main():
     ap.add_argument("--out", choices=["f32", "bf16"], default="f32",
                     help="output element type: f32 (the bench line) or bf16 (rounded from the "
                          "f32 result in the epilogue)")
+    ap.add_argument("--static-scratch", action="store_true",
+                    help="run the steps through dita_attn_step_static (the variant that "
+                         "allocates nothing; its scratch is a static device array)")
     ap.add_argument("--compact", action="store_true",
                     help="with --merge: after each run's merges, compact the cache onto one "
                          "slot per stored state (and expand it back before the next anchor)")
@@ -385,7 +388,8 @@ def main():
         pl = cache.plan()                             # host copy of the plan, no device wait
         step_masks.append((pl["mask"], pl["reuse_ptr"]))
         q, kk, v = dev[s]
-        cache.step(q, kk, v, out=out, lse=lse, stream=stream)
+        cache.step(q, kk, v, out=out, lse=lse, stream=stream,
+                   static_scratch=args.static_scratch)
         if s == 0:
             for g, sel in merge_sel:
                 cache.merge_groups(g, select=sel, stream=stream)
@@ -502,6 +506,8 @@ def main():
                    "partitions": cfg.num_partitions, "denoise_steps": S,
                    "schedule": schedule_desc,
                    "cache": f"{cfg.cache_dtype} O + f32 lse", "out": args.out,
+                   "entry_point": "dita_attn_step_static" if args.static_scratch
+                   else "dita_attn_step",
                    "layout": args.layout},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

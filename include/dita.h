@@ -256,6 +256,25 @@ dita_status dita_get_block_plan(const dita_cache* cache, uint8_t* mask, int32_t*
 dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, const void* v,
                            void* out, float* lse_out, void* hip_stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): dita_attn_step with the same arguments, kernels and
+ * results, which allocates nothing.  Its per-step scratch -- the transposed-V staging of the
+ * bf16 path and the step's work lists -- lives in a static device array of 128 MiB that each
+ * GPU the library runs on holds until the process ends, instead of in the cache's buffer
+ * (which still holds the cached states and counters); the work lists are copied from the
+ * handle's own pageable host buffer on `hip_stream`.  No hipMalloc, pinned host allocation,
+ * event or other allocating call is made.
+ *   - Every call on a GPU uses that GPU's one array, so calls that overlap on one GPU race:
+ *     order them on one stream (or synchronise between them).  Nothing in the array needs to
+ *     start at zero: each call writes all of what it reads.
+ *   - Not profiled (dita_set_profiling does not time it).
+ * Errors: those of dita_attn_step, and UNSUPPORTED when the step's scratch (B*H*DP*kt_pad*2
+ * bytes of transposed V, DP the padded head dim and kt_pad the token count with each
+ * partition padded to 64, plus the work lists) exceeds 128 MiB, or when the pending policy
+ * is a PLANNER step (its measurements are read back into host memory of the library's own). */
+dita_status dita_attn_step_static(dita_cache* cache, const void* q, const void* k,
+                                  const void* v, void* out, float* lse_out, void* hip_stream);
+
 /* Copy one cache slot out in plain layout (for checks and export), on `hip_stream`:
  *   o_out    device, n_i x D f32 row-major: the cached O_ij rows of query partition i
  *   lse_out  device, n_i f32: the cached lse_ij (natural log)

@@ -41,7 +41,7 @@ EXPORTED = ["dita_version", "dita_last_error", "dita_policy_mask", "dita_partiti
             "dita_attn_step", "dita_cache_read_slot", "dita_set_profiling", "dita_get_stats",
             "dita_planner_mask", "dita_get_planner_state", "dita_cache_merge_groups",
             "dita_cache_offload_bytes", "dita_cache_offload", "dita_cache_restore",
-            "dita_cache_compact_bytes", "dita_cache_compact",
+            "dita_attn_step_static", "dita_cache_compact_bytes", "dita_cache_compact",
             "dita_cache_expand"]
 
 
@@ -104,6 +104,7 @@ _sig = {
     "dita_set_block_policy": (ctypes.c_int, [_P, ctypes.POINTER(BlockPolicy)]),
     "dita_get_block_plan": (ctypes.c_int, [_P, _u8p, _i32p, _i32p, _i32p, _i32p, _i32p]),
     "dita_attn_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "dita_attn_step_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "dita_cache_read_slot": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "dita_set_profiling": (ctypes.c_int, [_P, ctypes.c_int32]),
@@ -292,12 +293,15 @@ class Cache:
         return {"mask": mask.reshape(P, P), "fresh_ptr": fp, "fresh_cols": fc[:fp[P]],
                 "reuse_ptr": rp, "reuse_cols": rc[:rp[P]], "counts": counts}
 
-    def step(self, q, k, v, out=None, lse=None, want_lse=True, stream=None):
+    def step(self, q, k, v, out=None, lse=None, want_lse=True, stream=None,
+             static_scratch=False):
         """Enqueue one step on `stream` (default: torch's current stream).  q/k/v are
         contiguous [B,H,N,D] (or [B,N,H,D]) device tensors; returns (out in the same layout,
         of the geometry's out dtype (f32 or bf16), lse [B,H,N] f32).  Caller-supplied `out` /
         `lse` must be of those dtypes, contiguous, of those shapes and on q's device; anything
-        else raises ValueError before a launch."""
+        else raises ValueError before a launch.
+        `static_scratch` calls dita_attn_step_static (the variant that allocates nothing; the
+        outputs must then be passed in, or are allocated here, by torch, before the call)."""
         import torch
         for t in (q, k, v):
             if not t.is_contiguous():
@@ -333,7 +337,8 @@ class Cache:
             out = torch.empty(shape, dtype=out_dt, device=q.device)
         if lse is None and want_lse:
             lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
-        _check(_lib.dita_attn_step(self._h, _P(q.data_ptr()), _P(k.data_ptr()), _P(v.data_ptr()),
+        fn = _lib.dita_attn_step_static if static_scratch else _lib.dita_attn_step
+        _check(fn(self._h, _P(q.data_ptr()), _P(k.data_ptr()), _P(v.data_ptr()),
                   _P(out.data_ptr()), _P(lse.data_ptr()) if lse is not None else None,
                   _P(_stream_handle(stream))))
         return out, lse

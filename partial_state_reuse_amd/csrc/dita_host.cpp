@@ -477,6 +477,7 @@ struct dita_cache {
   bool dev_init = false;
   bool counters_init = false;        // device counters cleared (first step of either kind)
   int device = -1;
+  std::vector<int32_t> host_plan;    // plan words of dita_attn_step_static (pageable memory)
   int32_t* staging = nullptr;        // pinned host, kPlanSlots * plan_bytes
   PlanSlot pslots[dita::kPlanSlots];
   uint64_t use_clock = 0;
@@ -635,6 +636,22 @@ dita_status device_init(dita_cache* c, hipStream_t s) {
   }
   c->device = dev;
   c->dev_init = true;
+  return ok();
+}
+
+// What dita_attn_step_static sets up: the device and the cleared counters, nothing allocated.
+dita_status static_init(dita_cache* c, hipStream_t s) {
+  if (!c->counters_init) {
+    dita_status st = hip_check(dita::launch_zero_counters(
+                                   (unsigned long long*)(c->dev + c->L.counters), 32, s),
+                               "counter clear launch");
+    if (st) return st;
+    c->counters_init = true;
+  }
+  if (c->device < 0) {
+    dita_status st = hip_check(hipGetDevice(&c->device), "hipGetDevice");
+    if (st) return st;
+  }
   return ok();
 }
 
@@ -815,6 +832,7 @@ dita_status dita_cache_alloc(const dita_geometry* geom, const uint8_t* active_ma
   c->w.assign((size_t)c->g.P * c->g.P, 0.f);
   c->head.resize((size_t)c->g.P * c->g.P);
   for (size_t b = 0; b < c->head.size(); ++b) c->head[b] = (int32_t)(b % c->g.P);
+  c->host_plan.assign(L.plan_bytes / 4, 0);
   c->full_slot_of = c->slot_of;
   c->full_num_slots = ns;
   *out = c;
@@ -942,8 +960,18 @@ dita_status dita_get_block_plan(const dita_cache* c, uint8_t* mask, int32_t* fre
   return ok();
 }
 
-dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const void* v,
-                           void* out, float* lse_out, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Device bytes dita_attn_step_static keeps in the static scratch: the transposed-V staging
+// (bf16 path), then the step's plan words.
+size_t static_vt_bytes(const Geo& g) {
+  return g.bf16() ? align_up((size_t)g.B * g.H * g.DP * (size_t)g.kt_pad * 2, 256) : 0;
+}
+
+dita_status step_impl(dita_cache* c, const void* q, const void* k, const void* v, void* out,
+                      float* lse_out, void* hip_stream, bool static_scratch) {
   if (!c) return fail(DITA_ERR_INVALID_ARGUMENT, "cache is NULL");
   if (!q || !k || !v || !out) return fail(DITA_ERR_INVALID_ARGUMENT, "q, k, v, out required");
   for (const void* p : {q, k, v, (const void*)out})
@@ -953,16 +981,47 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
     return fail(DITA_ERR_INVALID_ARGUMENT, "lse_out must be 4-byte aligned");
   if (c->offloaded) return fail(DITA_ERR_OFFLOADED, "the cache is offloaded; restore it first");
   if (!c->has_pending) return fail(DITA_ERR_NO_POLICY, "no block policy set for this step");
+  const bool measure = c->pending.planner_w || c->pending.planner_delta;
+  const size_t vt_bytes = static_vt_bytes(c->g);
+  if (static_scratch) {
+    if (measure)
+      return fail(DITA_ERR_UNSUPPORTED, "dita_attn_step_static: a PLANNER step reads its "
+                  "measurements back into host memory of the library's own; use dita_attn_step");
+    if (vt_bytes + c->L.plan_bytes > dita::kStaticScratchBytes)
+      return fail(DITA_ERR_UNSUPPORTED, "dita_attn_step_static: the step needs %zu bytes of "
+                  "scratch (transposed V %zu, work lists %zu), above the static maximum of %zu; "
+                  "use dita_attn_step", vt_bytes + c->L.plan_bytes, vt_bytes, c->L.plan_bytes,
+                  dita::kStaticScratchBytes);
+  }
   hipStream_t s = (hipStream_t)hip_stream;
-  dita_status st = device_init(c, s);
-  if (st) return st;
+  dita_status st = ok();
   int pslot = 0;
-  st = acquire_plan(c, c->pending, s, &pslot);
-  if (st) return st;
+  uint8_t* sbase = nullptr;
+  if (static_scratch) {
+    st = static_init(c, s);
+    if (st) return st;
+    void* sp = nullptr;
+    st = hip_check(dita::static_scratch_address(&sp), "hipGetSymbolAddress");
+    if (st) return st;
+    sbase = (uint8_t*)sp;
+    // the work lists go into the scratch on every call (another cache may have used it)
+    encode_plan(c, c->pending, c->host_plan.data());
+    st = hip_check(hipMemcpyAsync(sbase + vt_bytes, c->host_plan.data(), c->L.plan_bytes,
+                                  hipMemcpyHostToDevice, s), "plan upload");
+    if (st) return st;
+  } else {
+    st = device_init(c, s);
+    if (st) return st;
+    st = acquire_plan(c, c->pending, s, &pslot);
+    if (st) return st;
+  }
   dita::StepArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse_out = lse_out;
   fill_args(c, pslot, &a);
-  const bool measure = c->pending.planner_w || c->pending.planner_delta;
+  if (static_scratch) {
+    a.vt = sbase;
+    a.plan = (const int32_t*)(sbase + vt_bytes);
+  }
   if (measure) {
     st = planner_sync(c);   // no-op unless a measurement was never collected
     if (st) return st;
@@ -987,7 +1046,7 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
                     (int64_t)c->g.B * c->g.H <= 65535;
   if (snap) a.diag_snap = c->dev + c->L.snap;
   TimedStep* ts = nullptr;
-  if (c->profiling) {
+  if (c->profiling && !static_scratch) {
     ts = &c->timing[c->timing_next];
     st = drain_timing(c, *ts);   // the ring slot's previous step must have finished
     if (st) return st;
@@ -1055,9 +1114,11 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
     st = hip_check(hipEventRecord(c->meas_event, s), "hipEventRecord");
     if (st) return st;
   }
-  st = hip_check(hipEventRecord(c->pslots[pslot].event, s), "hipEventRecord");
-  if (st) return st;
-  c->pslots[pslot].event_recorded = true;
+  if (!static_scratch) {
+    st = hip_check(hipEventRecord(c->pslots[pslot].event, s), "hipEventRecord");
+    if (st) return st;
+    c->pslots[pslot].event_recorded = true;
+  }
   // bookkeeping (only after every enqueue succeeded)
   ++c->steps_done;
   ++c->steps_since_reset;
@@ -1085,6 +1146,20 @@ dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const vo
   c->has_last = true;
   c->has_pending = false;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+dita_status dita_attn_step(dita_cache* c, const void* q, const void* k, const void* v,
+                           void* out, float* lse_out, void* hip_stream) {
+  return step_impl(c, q, k, v, out, lse_out, hip_stream, false);
+}
+
+dita_status dita_attn_step_static(dita_cache* c, const void* q, const void* k, const void* v,
+                                  void* out, float* lse_out, void* hip_stream) {
+  return step_impl(c, q, k, v, out, lse_out, hip_stream, true);
 }
 
 dita_status dita_cache_read_slot(dita_cache* c, int32_t b, int32_t h, int32_t i, int32_t j,

@@ -124,4 +124,11 @@ hipError_t launch_remap_slots(const float* old_lse, const void* old_o, float* ne
                               int old_slots, int new_slots, int slot_rows,
                               size_t o_slot_bytes, hipStream_t s);
 
+// Device scratch of the allocation-free step (dita_attn_step_static): a file-scope device
+// array of this many bytes per GPU, holding the step's transposed-V staging and work lists.
+constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+// Its device address on the current device (looked up once per device with that device
+// current; the array's host-side name is not a device address).
+hipError_t static_scratch_address(void** out);
+
 }  // namespace dita

@@ -40,6 +40,7 @@
 // operand is one 16-byte LDS read.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <stdint.h>
 
 #include "dita_internal.h"
@@ -1246,6 +1247,30 @@ hipError_t launch_remap_slots(const float* old_lse, const void* old_o, float* ne
                      (const uint8_t*)old_o, new_lse, (uint8_t*)new_o, map, old_slots,
                      new_slots, slot_rows, (long long)o_slot_bytes);
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free step, for callers that cannot allocate (graph capture, tight
+// serving loops): each GPU the library runs on holds its own copy until the process ends.
+// Every call on a GPU shares it, so calls that overlap on one GPU race.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s) {

@@ -317,6 +317,40 @@ def test_step_rejects_bad_output_tensors_before_launch():
     c.free()
 
 
+def test_static_step_rejects_before_any_device_work():
+    """dita_attn_step_static refuses, before touching the device, a step whose scratch
+    exceeds its 128 MiB static array (the CFG workload's transposed V alone is 545 MB) and a
+    PLANNER step (its measurements need a read-back buffer); the 29-frame workload fits."""
+    lib = dita._lib
+    P = dita._P
+    for idx, want in ((5, "UNSUPPORTED"), (3, None)):
+        cfg = CONFIGS[idx]
+        c, g = fake_cache(cfg)
+        c.set_policy(dita.policy_from(cfg.policy(1)))
+        if want is None:
+            B, H, N = cfg.batch, cfg.heads, cfg.tokens
+            vt = B * H * 64 * sum(-(-int(n) // 64) * 64
+                                  for n in np.diff(dita.dita_partition_offsets(g)))
+            assert vt * 2 < (128 << 20)
+            c.free()
+            continue
+        rc = lib.dita_attn_step_static(c._h, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None)
+        assert dita.STATUS_NAMES[rc] == want
+        assert b"128" in lib.dita_last_error() or b"static maximum" in lib.dita_last_error()
+        assert c.stats()["steps_done"] == 0
+        c.free()
+    cfg = custom_config(name="planner-static", idx=80, heads=1, head_dim=64, frames=2,
+                        grid_h=4, grid_w=8, num_partitions=4, steps=2, qkv_dtype="bf16",
+                        cache_dtype="bf16")
+    c, g = fake_cache(cfg)
+    c.set_policy(dita.make_policy(kind=dita.POLICY_PLANNER, reuse_percent=50))
+    rc = lib.dita_attn_step_static(c._h, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None)
+    assert dita.STATUS_NAMES[rc] == "UNSUPPORTED"
+    assert b"PLANNER" in lib.dita_last_error()
+    assert c.stats()["steps_done"] == 0
+    c.free()
+
+
 def test_out_dtype_field():
     """The output dtype: f32 (the zero default) or bf16 with bf16 Q/K/V; it changes neither
     the buffer size nor the plan; bf16 with f32 inputs and unknown values are rejected."""
