@@ -57,9 +57,10 @@ struct Geo {
   int kt_pad = 0;
   int wg_rows = 0;
   int num_tiles = 0;                 // workgroups per (b, h): tail workgroups, then groups
-  int num_tail_wg = 0;               // tail workgroups per (b, h)
+  int num_tail_wg = 0;               // tail workgroups per (b, h): one per pack
   std::vector<int32_t> groups;       // per partition: row groups run by 4-wave workgroups
-  std::vector<int32_t> tails;        // {i, first row} per tail sub-tile (one per workgroup)
+  std::vector<int32_t> members;      // {i, first row, rows, first lane} per tail sub-tile
+  std::vector<int32_t> packs;        // {first member, members} per pack of tail sub-tiles
   int slot_rows = 0;
   bool bf16() const { return qkv == DITA_BF16; }
   // bytes per cached O element
@@ -147,8 +148,10 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
     const int sub = (rem + 31) / 32;
     if (rem > 0 && r.bf16() && sub <= dita::kMaxTailSubtiles) {
       for (int s = 0; s < sub; ++s) {
-        r.tails.push_back(p);
-        r.tails.push_back(full * r.wg_rows + 32 * s);
+        r.members.push_back(p);
+        r.members.push_back(full * r.wg_rows + 32 * s);
+        r.members.push_back(std::min(32, rem - 32 * s));
+        r.members.push_back(0);
       }
     } else if (rem > 0) {
       ++full;
@@ -156,7 +159,24 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
     r.groups[p] = full;
     num_groups += full;
   }
-  r.num_tail_wg = (int)(r.tails.size() / 2);
+  // Tail sub-tiles of consecutive partitions share one 32-row tile while their rows fit: a
+  // pack's lanes hold the rows of its members one after another.
+  {
+    const int nm = (int)(r.members.size() / 4);
+    int lanes = 32;
+    for (int m = 0; m < nm; ++m) {
+      const int rows = r.members[4 * m + 2];
+      if (lanes + rows > 32) {
+        r.packs.push_back(m);
+        r.packs.push_back(0);
+        lanes = 0;
+      }
+      r.members[4 * m + 3] = lanes;
+      lanes += rows;
+      r.packs.back() += 1;
+    }
+  }
+  r.num_tail_wg = (int)(r.packs.size() / 2);
   r.num_tiles = r.num_tail_wg + num_groups;
   r.kt_pad = r.poffs[r.P];
   r.slot_rows = (int)align_up(max_n, dita::kSlotRowAlign);
@@ -387,8 +407,9 @@ size_t offload_total_bytes(const Layout& L) {
 Layout compute_layout(const Geo& g, int num_slots) {
   Layout L;
   const size_t P = g.P;
-  const size_t words =
-      dita::kPlanHeader + 2 * (P + 1) + g.num_tiles + 2 * g.num_tail_wg + 4 * P + 2 * P * P;
+  const size_t nmem = g.members.size() / 4;
+  const size_t words = dita::kPlanHeader + 2 * (P + 1) + g.num_tiles + 4 * g.num_tail_wg +
+                       4 * nmem + 4 * P + 2 * P * P + 2 * g.num_tail_wg * P + nmem * P;
   L.counters = 0;
   L.plans = 256;
   L.plan_bytes = align_up(words * 4, 256);
@@ -553,7 +574,9 @@ void encode_plan(const dita_cache* c, const Plan& pl, int32_t* w) {
   for (int k = 0; k < g.num_tail_wg; ++k) w[at++] = dita::kTailFlag | k;
   for (int i = 0; i < P; ++i)
     for (int t = 0; t < g.groups[i]; ++t) w[at++] = (i << 16) | t;
-  for (int32_t v : g.tails) w[at++] = v;
+  const int packs_at = at;
+  at += 4 * g.num_tail_wg;
+  for (int32_t v : g.members) w[at++] = v;
   const int rows_at = at;
   int ent_at = rows_at + 4 * P;
   int e = 0;
@@ -572,6 +595,39 @@ void encode_plan(const dita_cache* c, const Plan& pl, int32_t* w) {
     w[rows_at + 4 * i + 3] = 0;
   }
   w[2] = e;
+  // Per pack, the union of its members' fresh blocks (ascending j), each with the slot of
+  // every member's block (i_m, j), or -1 where j is not fresh for member m.
+  const int union_at = ent_at + 2 * P * P;
+  const int slots_at = union_at + 2 * g.num_tail_wg * P;
+  int nu = 0, ns = 0;
+  std::vector<int32_t> slot_mj;
+  for (int k = 0; k < g.num_tail_wg; ++k) {
+    const int m0 = g.packs[2 * k], nm = g.packs[2 * k + 1];
+    slot_mj.assign((size_t)nm * P, -1);
+    std::vector<uint8_t> any(P, 0);
+    for (int m = 0; m < nm; ++m) {
+      const int i = g.members[4 * (m0 + m)];
+      for (int x = pl.fresh_ptr[i]; x < pl.fresh_ptr[i + 1]; ++x) {
+        const int j = pl.fresh_cols[x];
+        any[j] = 1;
+        slot_mj[(size_t)m * P + j] = c->slot_of[(size_t)i * P + j];
+      }
+    }
+    w[packs_at + 4 * k] = m0;
+    w[packs_at + 4 * k + 1] = nm;
+    w[packs_at + 4 * k + 2] = nu;
+    int cnt = 0;
+    for (int j = 0; j < P; ++j) {
+      if (!any[j]) continue;
+      w[union_at + 2 * nu] = j;
+      w[union_at + 2 * nu + 1] = ns;
+      for (int m = 0; m < nm; ++m) w[slots_at + ns + m] = slot_mj[(size_t)m * P + j];
+      ns += nm;
+      ++nu;
+      ++cnt;
+    }
+    w[packs_at + 4 * k + 3] = cnt;
+  }
 }
 
 void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
@@ -585,9 +641,12 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->off_offs = dita::kPlanHeader;
   a->off_poffs = a->off_offs + P + 1;
   a->off_tiles = a->off_poffs + P + 1;
-  a->off_tail = a->off_tiles + g.num_tiles;
-  a->off_rows = a->off_tail + 2 * g.num_tail_wg;
+  a->off_pack = a->off_tiles + g.num_tiles;
+  a->off_member = a->off_pack + 4 * g.num_tail_wg;
+  a->off_rows = a->off_member + (int32_t)g.members.size();
   a->off_ent = a->off_rows + 4 * P;
+  a->off_union = a->off_ent + 2 * P * P;
+  a->off_pslot = a->off_union + 2 * g.num_tail_wg * P;
   a->B = g.B; a->H = g.H; a->N = g.N; a->D = g.D; a->DP = g.DP; a->P = P;
   if (g.layout == DITA_LAYOUT_BNHD) {
     a->sB = (int64_t)g.N * g.H * g.D; a->sH = g.D; a->ld = g.H * g.D;

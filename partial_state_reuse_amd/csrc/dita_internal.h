@@ -28,22 +28,32 @@ inline int bf16_padded_dim(int D) {
 inline int bf16_wg_rows(int /*DP*/) { return kWaves * 32; }
 
 // Layout of one device plan (int32 words), as written by the host and read by the kernels:
-//   [0] num_tiles  [1] P  [2] E (entries)  [3] number of tail workgroups
+//   [0] num_tiles  [1] P  [2] E (entries)  [3] number of tail workgroups (packs)
 //   offs   at kPlanHeader                 : P+1 partition offsets o_p
 //   poffs  at kPlanHeader + (P+1)         : P+1 padded offsets of the transposed-V scratch
 //   tiles  at kPlanHeader + 2(P+1)        : num_tiles words: (i << 16) | group-in-partition
 //                                           for a workgroup of 4 waves on consecutive rows,
-//                                           or kTailFlag | k for tail workgroup k
-//   tails  at tiles + num_tiles           : 2 words per tail workgroup: {i, first row} of
-//                                           its 32-row sub-tile
-//   rows   at tails + 2 * tail workgroups : P x 4 words {first entry, #fresh, #reuse, 0}
+//                                           or kTailFlag | k for tail workgroup k (pack k)
+//   packs  at tiles + num_tiles           : 4 words per pack {first member, members, first
+//                                           union entry, union entries}
+//   members at packs + 4 * packs          : 4 words per member {i, first row, rows, first
+//                                           lane}: a tail sub-tile of partition i, whose rows
+//                                           the pack's lanes first lane.. hold
+//   rows   at members + 4 * members       : P x 4 words {first entry, #fresh, #reuse, 0}
 //   ent    at rows + 4P                   : E x 2 words {j, slot}; per row the fresh blocks
-//                                           (ascending j) precede the reused ones
+//                                           (ascending j) precede the reused ones (room for P^2)
+//   union  at ent + 2 P^2                 : 2 words per entry {j, first pack slot}: per pack
+//                                           the union of its members' fresh blocks, ascending j
+//                                           (room for P per pack)
+//   pslot  at union + 2 P * packs         : per union entry, one word per member of its pack:
+//                                           the slot of block (i_m, j), or -1 where j is not
+//                                           fresh for member m (room for P per member)
 constexpr int kPlanHeader = 4;
 constexpr int32_t kTailFlag = 1 << 30;
 // bf16 path: a partition whose last row group would leave at most this many of its 4 waves
-// with rows hands those rows to tail workgroups instead (one workgroup per 32-row sub-tile,
-// its 4 waves sharing the row's blocks).
+// with rows hands those rows to tail sub-tiles instead; the tail sub-tiles of consecutive
+// partitions are packed into 32-row tiles while their rows fit, one workgroup per pack, whose
+// 4 waves share the union of the members' blocks.
 constexpr int kMaxTailSubtiles = 2;
 
 struct StepArgs {
@@ -62,7 +72,8 @@ struct StepArgs {
                                  // (cumulative); [4] this step's fixed-reference rejection
                                  // flag (cleared by transpose_v)
   const int32_t* plan;       // device plan (layout above)
-  int32_t off_offs, off_poffs, off_tiles, off_tail, off_rows, off_ent;
+  int32_t off_offs, off_poffs, off_tiles, off_pack, off_member, off_rows, off_ent, off_union,
+      off_pslot;
   int32_t B, H, N, D, DP, P;
   // element strides of Q, K, V and out: (b, h, token n, d) at b*sB + h*sH + n*ld + d
   // ([B,H,N,D]: sB = H N D, sH = N D, ld = D; [B,N,H,D]: sB = N H D, sH = D, ld = H D)

@@ -430,40 +430,63 @@ __device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int 
   finish_rows<DP>(a, bh, o_i, n_i, row0, nf, nr, acc, m_row, l_row);
 }
 
-// Tail workgroup: one 32-row sub-tile left at the end of a partition.  Its 4 waves share the
-// row's blocks: wave w computes every 4th fresh block from the w-th and folds every 4th
-// reused state, each into a partial merge of its own; the partial merges are combined through
-// LDS (the merge is exact in any order) and wave 0 writes the rows.  K / V^T fragments come
-// straight from global memory (L2).  `lds` holds at least 2 x 64 x (2 + DP / 2) floats.
+// Tail workgroup k: a pack of tail sub-tiles -- the rows left at the ends of consecutive
+// partitions, at most 32 in all -- whose lane l holds row r_l of partition i_l (its member's
+// rows follow one another over the lanes; lanes past the pack's rows hold none).  The 4
+// waves split the union of the members' fresh blocks (wave w takes every 4th from the w-th):
+// a wave computes its blocks over all 32 rows, and a lane keeps a block only where it is fresh
+// for its own partition, storing the state to that block's slot and folding it into its row's
+// partial merge.  Reused states are split alike (entry e of each row's reuse list for e = w,
+// w + 4, ...), every lane reading its own partition's slot.  K / V^T fragments come straight
+// from global memory (L2); the partial merges are combined through LDS (exact in any order)
+// and wave 0 writes the rows.  `lds` holds at least 2 x 64 x (2 + DP / 2) floats.
 template <int DP, bool MEASURE, bool FP8>
-__device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, float* lds) {
+__device__ __forceinline__ void tail_pack(const StepArgs& a, int bh, int k, float* lds) {
   constexpr int NKC = DP / 16, NDT = DP / 32;
+  typedef typename CacheElem<FP8>::type CT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h32 = lane >> 5, l32 = lane & 31;
   const cint* plan = as_const(a.plan);
   const cint* offs = plan + a.off_offs;
   const cint* poffs = plan + a.off_poffs;
-  const cint* te = plan + a.off_tail + 2 * k;
-  const int i = te[0], row0 = te[1];
-  const int o_i = offs[i], n_i = offs[i + 1] - o_i;
-  const int myrow = row0 + l32;
-  const cint* rinfo = plan + a.off_rows + 4 * i;
-  const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
-  const cint* ent = plan + a.off_ent;
+  const cint* pk = plan + a.off_pack + 4 * k;
+  const int m0 = pk[0], nm = pk[1], u0 = pk[2], nu = pk[3];
+  // this lane's member (pack index), partition and row
+  int mem = 0, i = 0, r = 0, rfirst = 0;
+  bool valid = false;
+  for (int m = 0; m < nm; ++m) {                 // uniform loop, per-lane choice
+    const cint* me = plan + a.off_member + 4 * (m0 + m);
+    const int lane0 = me[3], rows = me[2];
+    if (l32 >= lane0 && l32 < lane0 + rows) {
+      mem = m;
+      i = me[0];
+      r = me[1] + (l32 - lane0);
+      rfirst = me[1];
+      valid = true;
+    }
+  }
+  const int* offs_v = a.plan + a.off_offs;        // per-lane reads of the plan
+  const int* rinfo = a.plan + a.off_rows + 4 * i;
+  const int o_i = offs_v[i];
+  const int e0 = rinfo[0], nf = rinfo[1], nr = valid ? rinfo[2] : 0;
+  const cint* uent = plan + a.off_union;
+  const int* pslot = a.plan + a.off_pslot;
+  const int* ent_v = a.plan + a.off_ent;
   const float sc = a.scale_log2;
   const float inv_sc = 1.0f / sc;
   const int paddr = partner_addr();
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // this lane's position in a slot's fragment order: sub-tile r / 32, lane (h32, r % 32)
+  const size_t frag = (size_t)(r & ~31) * DP + (size_t)(h32 * 32 + (r & 31)) * 16;
 
   bf16x8 qf[NKC];
   {
     const uint16_t* Q = (const uint16_t*)a.q + head_base(a, bh);
-    const bool ok = myrow < n_i;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int d0 = kc * 16 + h32 * 8;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok && d0 < a.D) v = ld16(Q + (size_t)(o_i + myrow) * a.ld + d0);
+      if (valid && d0 < a.D) v = ld16(Q + (size_t)(o_i + r) * a.ld + d0);
       qf[kc] = as_bf16x8(v);
     }
   }
@@ -472,21 +495,21 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x16){};
   float m_row = kNegInf, l_row = 0.f;
   const size_t slot_elems = (size_t)a.slot_rows * DP;
-  typename CacheElem<FP8>::type* cache_o = (typename CacheElem<FP8>::type*)a.cache_o;
+  CT* cache_o = (CT*)a.cache_o;
   const uint16_t* Kg = (const uint16_t*)a.k + head_base(a, bh);
   const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
 
-  // ---------------- fresh blocks ----------------
-  for (int e = wave; e < nf; e += kWaves) {
-    const int j = ent[2 * (e0 + e)], slot = ent[2 * (e0 + e) + 1];
+  // ---------------- fresh blocks: the union of the members' ----------------
+  for (int t = wave; t < nu; t += kWaves) {
+    const int j = uent[2 * (u0 + t)], sb = uent[2 * (u0 + t) + 1];
+    const int slot = valid ? pslot[sb + mem] : -1;
+    const bool mine = slot >= 0;                 // j is fresh for this lane's partition
     const int o_j = offs[j], n_j = offs[j + 1] - o_j, po_j = poffs[j];
     f32x16 bacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) bacc[dt] = (f32x16){};
     float m_b = kNegInf, l_b = 0.f, thr = kNegInf;
     for (int kbase = 0; kbase < n_j; kbase += 32) {
-      // K fragments: row key_of_row(l32) of the unit (clamped into the block: keys past its
-      // end are masked below), dims kc*16 + 8*h32 (clamped below D, where Q is zero)
       bf16x8 kf[NKC];
       {
         const int key = min(kbase + key_of_row(l32), n_j - 1);
@@ -498,9 +521,6 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], s, 0, 0, 0);
-      // V^T fragments: rows dt*32 + l32, keys c*16 + 8*h32 of the unit (the scratch is zero
-      // padded to whole 64-key tiles per partition, so these stay in bounds); requested
-      // after the K fragments are consumed, in flight during the softmax
       f16x8 vf[NDT][2];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -509,16 +529,14 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
           vf[dt][c] = as_f16x8(ld16(VTg + (size_t)(dt * 32 + l32) * a.kt_pad + po_j + kbase + c * 16 + h32 * 8));
       if (kbase + 32 > n_j) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 16 * (r >> 3) + 8 * h32 + (r & 7);
-          if (key >= n_j) s[r] = kNegInf;
+        for (int q = 0; q < 16; ++q) {
+          const int key = kbase + 16 * (q >> 3) + 8 * h32 + (q & 7);
+          if (key >= n_j) s[q] = kNegInf;
         }
       }
-      // this lane's max over its 16 keys against the rescale threshold (in score units);
-      // the query's exact max over both lanes is formed only when a rescale is due
       float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-      for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1 < 16 ? r + 1 : r]);
+      for (int q = 3; q < 16; q += 2) mx = fmaxf(fmaxf(mx, s[q]), s[q + 1 < 16 ? q + 1 : q]);
       if (__any(mx > thr)) {
         const float m_new = fmaxf(m_b, max_halves(mx, paddr) * sc);
         const float alpha = fast_exp2(m_b - m_new);
@@ -530,8 +548,8 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
       }
       f16x8 pf[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pf[r >> 3][r & 7] = (_Float16)fast_exp2(__builtin_fmaf(s[r], sc, -m_b));
+      for (int q = 0; q < 16; ++q)
+        pf[q >> 3][q & 7] = (_Float16)fast_exp2(__builtin_fmaf(s[q], sc, -m_b));
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -545,25 +563,147 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
         for (int c = 0; c < 2; ++c)
           bacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[dt][c], pf[c], bacc[dt], 0, 0, 0);
     }
-    block_end<NDT, MEASURE, FP8>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
-                   cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
-                   acc, m_row, l_row, j == i, n_i, i, bh);
+    // block end, for the lanes whose partition has j fresh: the normalised state to the slot
+    // (fragment order, at this lane's row), the lse, and the fold into the row's merge
+    const float lsum = sum_halves(l_b, paddr);
+    const float inv = 1.0f / lsum;
+    const float lse2 = m_b + fast_log2(lsum);
+    const bool diag = MEASURE && mine && j == i;
+    const size_t sbase = (size_t)bh * a.num_slots + (mine ? slot : 0);
+    CT* dst = cache_o + sbase * slot_elems + frag;
+    const CT* old = MEASURE && a.diag_snap
+        ? (const CT*)a.diag_snap + ((size_t)bh * a.P + i) * slot_elems + frag
+        : dst;
+    float sq = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      bacc[dt] *= inv;
+      if constexpr (FP8) {
+        const u32x4 w = fp8_pack16(bacc[dt]);
+        if (diag) {
+          float nv[16], ov[16];
+          fp8_unpack16(w, nv);
+          fp8_unpack16(ld16(old + dt * 1024), ov);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int d = dt * 32 + 8 * (q >> 2) + 4 * h32 + (q & 3);
+            const float df = nv[q] - ov[q];
+            if (d < a.D) sq = __builtin_fmaf(df, df, sq);
+          }
+        }
+        if (mine) st16(dst + dt * 1024, w);
+      } else {
+        u32x4 w0, w1;
+        uint16_t* e0p = (uint16_t*)&w0;
+        uint16_t* e1p = (uint16_t*)&w1;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          e0p[q] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][q]);
+          e1p[q] = __builtin_bit_cast(uint16_t, (__bf16)bacc[dt][q + 8]);
+        }
+        if (diag) {
+          const bf16x8 n0 = as_bf16x8(w0), n1 = as_bf16x8(w1);
+          const bf16x8 p0 = as_bf16x8(ld16(old + dt * 1024)), p1 = as_bf16x8(ld16(old + dt * 1024 + 8));
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int d = dt * 32 + 8 * (q >> 2) + 4 * h32 + (q & 3);
+            const float df = q < 8 ? (float)n0[q] - (float)p0[q] : (float)n1[q - 8] - (float)p1[q - 8];
+            if (d < a.D) sq = __builtin_fmaf(df, df, sq);
+          }
+        }
+        if (mine) {
+          st16(dst + dt * 1024, w0);
+          st16(dst + dt * 1024 + 8, w1);
+        }
+      }
+    }
+    if constexpr (MEASURE) {
+      // the diagonal member's squared change: one sub-tile of partition j
+      const unsigned long long dm = __ballot(diag);
+      if (dm) {
+        sq = wave_sum(sq);
+        if (lane == (int)__builtin_ctzll(dm))
+          a.delta_part[((size_t)bh * a.P + j) * a.delta_stride + (rfirst >> 5)] = sq;
+      }
+    }
+    if (mine) {
+      if (h32 == 0) a.cache_lse[sbase * a.slot_rows + r] = lse2 * kLn2;
+      const float mn = fmaxf(m_row, lse2);
+      const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * fa + bacc[dt] * fb;
+      l_row = l_row * fa + fb;
+      m_row = mn;
+    }
   }
-  reuse_fold<DP, FP8, kWaves>(a, bh, row0, e0, nf + wave, nf + nr, acc, m_row, l_row);
+
+  // ---------------- reused states: entry e of each row's list, e = wave, wave + 4, ... ----
+  {
+    int nr_max = nr;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) nr_max = max(nr_max, __shfl_xor(nr_max, off));
+    constexpr int RB = 4;
+    constexpr int NW = FP8 ? 1 : 2;
+    for (int e = wave; e < nr_max; e += RB * kWaves) {
+      u32x4 raw[RB][NDT][NW];
+      float lse2[RB];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int ee = e + q * kWaves;
+        if (ee < nr) {
+          const int rslot = ent_v[2 * (e0 + nf + ee) + 1];
+          const size_t rb = (size_t)bh * a.num_slots + rslot;
+          lse2[q] = a.cache_lse[rb * a.slot_rows + r];
+          const CT* src = cache_o + rb * slot_elems + frag;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int w = 0; w < NW; ++w) raw[q][dt][w] = ld16(src + dt * 1024 + w * 8);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int ee = e + q * kWaves;
+        if (ee < nr) {
+          const float l2 = lse2[q] * kLog2e;
+          const float mn = fmaxf(m_row, l2);
+          const float fa = fast_exp2(m_row - mn), fb = fast_exp2(l2 - mn);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            float v[16];
+            if constexpr (FP8) {
+              fp8_unpack16(raw[q][dt][0], v);
+            } else {
+              const bf16x8 lo = as_bf16x8(raw[q][dt][0]), hi = as_bf16x8(raw[q][dt][NW - 1]);
+#pragma unroll
+              for (int x = 0; x < 8; ++x) {
+                v[x] = (float)lo[x];
+                v[x + 8] = (float)hi[x];
+              }
+            }
+#pragma unroll
+            for (int x = 0; x < 16; ++x) acc[dt][x] = acc[dt][x] * fa + v[x] * fb;
+          }
+          l_row = l_row * fa + fb;
+          m_row = mn;
+        }
+      }
+    }
+  }
 
   // combine the partial merges: waves 2, 3 into 0, 1, then 1 into 0
   constexpr int W = 2 + NDT * 16;               // floats per lane
-  auto put = [&](int slot) {
-    float* p = lds + (size_t)slot * W * 64 + lane;
+  auto put = [&](int sl) {
+    float* p = lds + (size_t)sl * W * 64 + lane;
     p[0] = m_row;
     p[64] = l_row;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[(2 + dt * 16 + r) * 64] = acc[dt][r];
+      for (int x = 0; x < 16; ++x) p[(2 + dt * 16 + x) * 64] = acc[dt][x];
   };
-  auto take = [&](int slot) {
-    const float* p = lds + (size_t)slot * W * 64 + lane;
+  auto take = [&](int sl) {
+    const float* p = lds + (size_t)sl * W * 64 + lane;
     const float m2 = p[0], l2 = p[64];
     const float mn = fmaxf(m_row, m2);
     const float fa = m_row == kNegInf ? 0.f : fast_exp2(m_row - mn);
@@ -571,7 +711,7 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] = acc[dt][r] * fa + p[(2 + dt * 16 + r) * 64] * fb;
+      for (int x = 0; x < 16; ++x) acc[dt][x] = acc[dt][x] * fa + p[(2 + dt * 16 + x) * 64] * fb;
     l_row = l_row * fa + l2 * fb;
     m_row = mn;
   };
@@ -581,9 +721,40 @@ __device__ __forceinline__ void tail_group(const StepArgs& a, int bh, int k, flo
   __syncthreads();
   if (wave == 1) put(0);
   __syncthreads();
-  if (wave == 0) {
-    take(0);
-    finish_rows<DP>(a, bh, o_i, n_i, row0, nf, nr, acc, m_row, l_row);
+  if (wave != 0) return;
+  take(0);
+  if (valid) {
+    const float inv = 1.0f / l_row;
+    const size_t orow = head_base(a, bh) + (size_t)(o_i + r) * a.ld;   // element offset
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = dt * 32 + 8 * q4 + 4 * h32;
+        if (d < a.D) {
+          f32x4 v = {acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
+                     acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv};
+          if (a.out_bf16) {
+            uint16_t e[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) e[t] = __builtin_bit_cast(uint16_t, (__bf16)v[t]);
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 w = {(uint32_t)e[0] | ((uint32_t)e[1] << 16),
+                             (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
+            *(u32x2*)((uint16_t*)a.out + orow + d) = w;
+          } else {
+            *(f32x4*)((float*)a.out + orow + d) = v;
+          }
+        }
+      }
+    }
+    if (a.lse_out && h32 == 0)
+      a.lse_out[(size_t)bh * a.N + o_i + r] = (m_row + fast_log2(l_row)) * kLn2;
+    // block counts, once per partition: by the lane holding its first row, if it is a tail row
+    if (r == 0 && h32 == 0 && !a.fixup) {
+      atomicAdd(&a.counters[0], (unsigned long long)nf);
+      atomicAdd(&a.counters[1], (unsigned long long)nr);
+    }
   }
 }
 
@@ -626,7 +797,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const cint* poffs = plan + a.off_poffs;
   const int packed = plan[a.off_tiles + tix];
   if (packed & kTailFlag) {                     // workgroup-uniform
-    tail_group<DP, MEASURE, FP8>(a, bh, packed & 0xffff, (float*)smem);
+    tail_pack<DP, MEASURE, FP8>(a, bh, packed & 0xffff, (float*)smem);
     return;
   }
   const int i = packed >> 16, t = packed & 0xffff;
