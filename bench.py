@@ -206,15 +206,23 @@ def time_offload(dita, cache, stream):
 
 
 def cpu_model():
-    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    """The host CPU as /proc/cpuinfo names it: model name, then family / model / stepping
+    (which identify the generation where the name is generic), or None."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                          # the first processor's block only
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
     except OSError:
-        pass
-    return None
+        return None
+    name = fields.get("model name")
+    if name is None:
+        return None
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return name + (f" ({', '.join(ids)})" if ids else "")
 
 
 def describe_policy(pol, P):
