@@ -24,8 +24,8 @@
  *   - Pointers marked "device" are HIP device addresses on the calling thread's current
  *     device; "host" pointers are ordinary memory.  The library never allocates device
  *     memory: the caller provides one buffer of dita_cache_required_bytes bytes, which
- *     holds the state cache, the per-step work lists, a transposed-V scratch and the
- *     device counters.  The caller owns all device memory and the stream and keeps them
+ *     holds the state cache, the per-step work lists, a transposed-V scratch, the partial
+ *     merges of split row groups (below) and the device counters.  The caller owns all device memory and the stream and keeps them
  *     alive until the stream has passed the step.  A handle allocates pinned host memory
  *     of its own (plan uploads, the planner's read-back, merge jobs), released by
  *     dita_cache_free.
@@ -252,6 +252,14 @@ dita_status dita_get_block_plan(const dita_cache* cache, uint8_t* mask, int32_t*
  * Fresh blocks are recomputed and written back to their slots; reused blocks are read from
  * theirs.  Stream-asynchronous: returns after enqueueing.  On success the pending policy is
  * consumed, written slots become valid and the step counter advances.
+ * bf16 path: the row groups that run last on each of the GPU's 8 XCDs are split in two
+ * workgroups (half of the row's blocks each) whose partial merges a small second kernel
+ * combines, so the grid ends on short workgroups; their rows' sums are associated
+ * differently, so outputs may differ in the last bits from a run without splits.  By
+ * default an eighth of an XCD's concurrent workgroups are split when the step runs two
+ * rounds of workgroups or more; the environment variable DITA_SPLITS_PER_XCD, read when a
+ * geometry is resolved (by dita_cache_required_bytes and dita_cache_alloc), sets the number
+ * of split row groups per XCD instead (0: none; at most 128).
  * Errors: INVALID_ARGUMENT, NO_POLICY, DEVICE. */
 dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, const void* v,
                            void* out, float* lse_out, void* hip_stream);
@@ -259,7 +267,8 @@ dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, cons
 /* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): dita_attn_step with the same arguments, kernels and
  * results, which allocates nothing.  Its per-step scratch -- the transposed-V staging of the
- * bf16 path and the step's work lists -- lives in a static device array of 128 MiB that each
+ * bf16 path, the step's work lists and the split row groups' partial merges -- lives in a
+ * static device array of 128 MiB that each
  * GPU the library runs on holds until the process ends, instead of in the cache's buffer
  * (which still holds the cached states and counters); the work lists are copied from the
  * handle's own pageable host buffer on `hip_stream`.  No hipMalloc, pinned host allocation,
@@ -270,7 +279,8 @@ dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, cons
  *   - Not profiled (dita_set_profiling does not time it).
  * Errors: those of dita_attn_step, and UNSUPPORTED when the step's scratch (B*H*DP*kt_pad*2
  * bytes of transposed V, DP the padded head dim and kt_pad the token count with each
- * partition padded to 64, plus the work lists) exceeds 128 MiB, or when the pending policy
+ * partition padded to 64, plus the work lists and 2 x 256 x (2 + DP/2) x 4 bytes per split
+ * row group) exceeds 128 MiB, or when the pending policy
  * is a PLANNER step (its measurements are read back into host memory of the library's own). */
 dita_status dita_attn_step_static(dita_cache* cache, const void* q, const void* k,
                                   const void* v, void* out, float* lse_out, void* hip_stream);

@@ -12,6 +12,7 @@
 #include "dita.h"
 
 #include <algorithm>
+#include <cstdlib>
 #include <array>
 #include <cmath>
 #include <cstdarg>
@@ -61,11 +62,85 @@ struct Geo {
   std::vector<int32_t> groups;       // per partition: row groups run by 4-wave workgroups
   std::vector<int32_t> members;      // {i, first row, rows, first lane} per tail sub-tile
   std::vector<int32_t> packs;        // {first member, members} per pack of tail sub-tiles
+  // bf16 path: the step's workgroups in logical order, {b*H + h, tile word} each, and the
+  // split row groups {b*H + h, tile word of the group}
+  std::vector<int32_t> items;
+  std::vector<int32_t> splits;
+  int num_items = 0, num_splits = 0;
   int slot_rows = 0;
   bool bf16() const { return qkv == DITA_BF16; }
   // bytes per cached O element
   size_t cache_esz() const { return cache_o == DITA_FP8_E4M3 ? 1 : (cache_o == DITA_BF16 ? 2 : 4); }
 };
+
+// The bf16 step's workgroups in logical order.  Workgroup ids are dealt round-robin to the 8
+// XCDs and the kernel maps XCD x's ids onto the x-th contiguous range of logical indices
+// (xcd_remap), so XCD x runs its range front to back.  The (b, h) tiles are laid out head
+// after head; in each XCD's range the last K row groups are split in two halves, which
+// become adjacent workgroups of about half the length, so that the grid's end on that XCD
+// is made of short workgroups.  K is an eighth of the XCD's concurrent workgroups (32 CUs
+// x 3 at DP = 64, x 2 above), and 0 when the range holds fewer than two rounds of them or
+// when some range has fewer than K row groups (not tail workgroups) to split.  The
+// environment variable DITA_SPLITS_PER_XCD, read when a geometry is resolved, sets K
+// instead (0 turns the splitting off; at most kMaxSplits / 8).
+void build_items(Geo* r) {
+  const int64_t G0 = (int64_t)r->B * r->H * r->num_tiles;
+  std::vector<int32_t> word(r->num_tiles);   // tile words of one (b, h), in order
+  {
+    int t = 0;
+    for (int k = 0; k < r->num_tail_wg; ++k) word[t++] = dita::kTailFlag | k;
+    for (int i = 0; i < r->P; ++i)
+      for (int g = 0; g < r->groups[i]; ++g) word[t++] = (i << 16) | g;
+  }
+  const int per_cu = r->DP == 64 ? 3 : 2;
+  const int slots = 32 * per_cu;
+  int K = G0 / 8 >= 2 * slots ? slots / 8 : 0;
+  if (const char* e = std::getenv("DITA_SPLITS_PER_XCD")) K = std::max(0, std::atoi(e));
+  K = std::min(K, dita::kMaxSplits / 8);
+  for (;; K = 0) {
+    const int64_t G = G0 + 8 * (int64_t)K;
+    r->items.clear();
+    r->splits.clear();
+    r->items.reserve(2 * G);
+    int64_t cursor = 0;               // next tile of the regular (head-major) order
+    bool short_of_groups = false;
+    for (int x = 0; x < 8 && !short_of_groups; ++x) {
+      const int64_t chunk = G / 8 + (x < G % 8 ? 1 : 0);
+      const int64_t n = chunk - K;    // regular tiles of this XCD's range
+      std::vector<uint8_t> split_here(n, 0);
+      int need = K;
+      for (int64_t y = n - 1; y >= 0 && need > 0; --y)
+        if (!(word[(cursor + y) % r->num_tiles] & dita::kTailFlag)) {
+          split_here[y] = 1;
+          --need;
+        }
+      if (need > 0) {                 // too few row groups to split here: split none at all
+        short_of_groups = true;
+        break;
+      }
+      for (int64_t y = 0; y < n; ++y) {
+        const int64_t t = cursor + y;
+        const int32_t bh = (int32_t)(t / r->num_tiles), w = word[t % r->num_tiles];
+        if (!split_here[y]) {
+          r->items.push_back(bh);
+          r->items.push_back(w);
+          continue;
+        }
+        const int sidx = (int)(r->splits.size() / 2);
+        r->splits.push_back(bh);
+        r->splits.push_back(w);
+        for (int half = 0; half < 2; ++half) {
+          r->items.push_back(bh);
+          r->items.push_back(dita::kSplitFlag | (sidx << 1) | half);
+        }
+      }
+      cursor += n;
+    }
+    if (!short_of_groups || K == 0) break;
+  }
+  r->num_items = (int)(r->items.size() / 2);
+  r->num_splits = (int)(r->splits.size() / 2);
+}
 
 dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
   if (!g) return fail(DITA_ERR_INVALID_ARGUMENT, "geometry is NULL");
@@ -180,6 +255,12 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
   r.num_tiles = r.num_tail_wg + num_groups;
   r.kt_pad = r.poffs[r.P];
   r.slot_rows = (int)align_up(max_n, dita::kSlotRowAlign);
+  if (r.bf16()) {
+    const int64_t G0 = (int64_t)r.B * r.H * r.num_tiles;
+    if (G0 + dita::kMaxSplits >= ((int64_t)1 << 28))
+      return fail(DITA_ERR_SHAPE, "too many workgroups (%lld)", (long long)G0);
+    build_items(&r);
+  }
   *out = std::move(r);
   return ok();
 }
@@ -392,8 +473,13 @@ void build_lists(int P, const std::vector<uint8_t>& M, const uint8_t* covered,
 
 struct Layout {
   size_t counters = 0, plans = 0, plan_bytes = 0, vt = 0, lse = 0, o = 0, delta = 0, pout = 0,
-         wpart = 0, merge = 0, merge_bytes = 0, snap = 0, total = 0;
+         wpart = 0, merge = 0, merge_bytes = 0, snap = 0, split_ws = 0, total = 0;
 };
+
+// Bytes of the split halves' partial merges: per half, 256 threads x (m, l, DP / 2 values).
+size_t split_ws_bytes(const Geo& g) {
+  return (size_t)g.num_splits * 2 * 256 * (2 + g.DP / 2) * 4;
+}
 
 // The persistent part of the device buffer, as offloaded to the host: the counters, then
 // the cached lse and O of every slot (the [lse, delta) span of the layout).  The rest (work
@@ -409,7 +495,8 @@ Layout compute_layout(const Geo& g, int num_slots) {
   const size_t P = g.P;
   const size_t nmem = g.members.size() / 4;
   const size_t words = dita::kPlanHeader + 2 * (P + 1) + g.num_tiles + 4 * g.num_tail_wg +
-                       4 * nmem + 4 * P + 2 * P * P + 2 * g.num_tail_wg * P + nmem * P;
+                       4 * nmem + 4 * P + 2 * P * P + 2 * g.num_tail_wg * P + nmem * P +
+                       g.items.size() + g.splits.size();
   L.counters = 0;
   L.plans = 256;
   L.plan_bytes = align_up(words * 4, 256);
@@ -437,6 +524,9 @@ Layout compute_layout(const Geo& g, int num_slots) {
   // bf16: snapshot of the diagonal slots' cached O, taken before each measuring step
   L.snap = at;
   if (g.bf16()) at = align_up(at + bh * P * (size_t)g.slot_rows * g.DP * esz, 256);
+  // bf16: partial merges of the split row groups' halves
+  L.split_ws = at;
+  at = align_up(at + split_ws_bytes(g), 256);
   L.total = at;
   return L;
 }
@@ -628,6 +718,9 @@ void encode_plan(const dita_cache* c, const Plan& pl, int32_t* w) {
     }
     w[packs_at + 4 * k + 3] = cnt;
   }
+  int at2 = slots_at + (int)(g.members.size() / 4) * P;
+  for (int32_t v : g.items) w[at2++] = v;
+  for (int32_t v : g.splits) w[at2++] = v;
 }
 
 void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
@@ -647,6 +740,11 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->off_ent = a->off_rows + 4 * P;
   a->off_union = a->off_ent + 2 * P * P;
   a->off_pslot = a->off_union + 2 * g.num_tail_wg * P;
+  a->off_items = a->off_pslot + (int32_t)(g.members.size() / 4) * P;
+  a->off_splits = a->off_items + (int32_t)g.items.size();
+  a->num_items = g.num_items;
+  a->num_splits = g.num_splits;
+  a->split_ws = (float*)(c->dev + c->L.split_ws);
   a->B = g.B; a->H = g.H; a->N = g.N; a->D = g.D; a->DP = g.DP; a->P = P;
   if (g.layout == DITA_LAYOUT_BNHD) {
     a->sB = (int64_t)g.N * g.H * g.D; a->sH = g.D; a->ld = g.H * g.D;
@@ -1024,7 +1122,7 @@ dita_status dita_get_block_plan(const dita_cache* c, uint8_t* mask, int32_t* fre
 namespace {
 
 // Device bytes dita_attn_step_static keeps in the static scratch: the transposed-V staging
-// (bf16 path), then the step's plan words.
+// (bf16 path), then the step's plan words, then the split halves' partial merges.
 size_t static_vt_bytes(const Geo& g) {
   return g.bf16() ? align_up((size_t)g.B * g.H * g.DP * (size_t)g.kt_pad * 2, 256) : 0;
 }
@@ -1046,10 +1144,12 @@ dita_status step_impl(dita_cache* c, const void* q, const void* k, const void* v
     if (measure)
       return fail(DITA_ERR_UNSUPPORTED, "dita_attn_step_static: a PLANNER step reads its "
                   "measurements back into host memory of the library's own; use dita_attn_step");
-    if (vt_bytes + c->L.plan_bytes > dita::kStaticScratchBytes)
+    const size_t ws_bytes = split_ws_bytes(c->g);
+    if (vt_bytes + c->L.plan_bytes + ws_bytes > dita::kStaticScratchBytes)
       return fail(DITA_ERR_UNSUPPORTED, "dita_attn_step_static: the step needs %zu bytes of "
-                  "scratch (transposed V %zu, work lists %zu), above the static maximum of %zu; "
-                  "use dita_attn_step", vt_bytes + c->L.plan_bytes, vt_bytes, c->L.plan_bytes,
+                  "scratch (transposed V %zu, work lists %zu, split partial merges %zu), above "
+                  "the static maximum of %zu; use dita_attn_step",
+                  vt_bytes + c->L.plan_bytes + ws_bytes, vt_bytes, c->L.plan_bytes, ws_bytes,
                   dita::kStaticScratchBytes);
   }
   hipStream_t s = (hipStream_t)hip_stream;
@@ -1080,6 +1180,7 @@ dita_status step_impl(dita_cache* c, const void* q, const void* k, const void* v
   if (static_scratch) {
     a.vt = sbase;
     a.plan = (const int32_t*)(sbase + vt_bytes);
+    a.split_ws = (float*)(sbase + vt_bytes + c->L.plan_bytes);
   }
   if (measure) {
     st = planner_sync(c);   // no-op unless a measurement was never collected

@@ -48,8 +48,21 @@ inline int bf16_wg_rows(int /*DP*/) { return kWaves * 32; }
 //   pslot  at union + 2 P * packs         : per union entry, one word per member of its pack:
 //                                           the slot of block (i_m, j), or -1 where j is not
 //                                           fresh for member m (room for P per member)
+//   items  at pslot + P * members         : bf16 path: 2 words per workgroup {b*H + h, tile
+//                                           word}, in the order of the logical workgroup index
+//                                           (after the XCD remap); the tile word is a group or
+//                                           tail word as above, or kSplitFlag | (s << 1) | half
+//                                           for half of split row group s
+//   splits at items + 2 * items           : 2 words per split row group {b*H + h, group word}
 constexpr int kPlanHeader = 4;
 constexpr int32_t kTailFlag = 1 << 30;
+// bf16 path: the row groups dispatched last on each XCD run as two workgroups each (the
+// first and second half of the row's fresh blocks and of its reused states), so that the
+// grid ends on workgroups of half the length; each half leaves its partial merge of the rows
+// in a workspace and merge_splits combines the two and writes the rows.
+constexpr int32_t kSplitFlag = 1 << 29;
+// at most this many split row groups per step
+constexpr int kMaxSplits = 1024;
 // bf16 path: a partition whose last row group would leave at most this many of its 4 waves
 // with rows hands those rows to tail sub-tiles instead; the tail sub-tiles of consecutive
 // partitions are packed into 32-row tiles while their rows fit, one workgroup per pack, whose
@@ -73,13 +86,18 @@ struct StepArgs {
                                  // flag (cleared by transpose_v)
   const int32_t* plan;       // device plan (layout above)
   int32_t off_offs, off_poffs, off_tiles, off_pack, off_member, off_rows, off_ent, off_union,
-      off_pslot;
+      off_pslot, off_items, off_splits;
   int32_t B, H, N, D, DP, P;
   // element strides of Q, K, V and out: (b, h, token n, d) at b*sB + h*sH + n*ld + d
   // ([B,H,N,D]: sB = H N D, sH = N D, ld = D; [B,N,H,D]: sB = N H D, sH = D, ld = H D)
   int64_t sB, sH;
   int32_t ld;
   int32_t num_tiles;         // workgroup tiles per (b, h)
+  int32_t num_items;         // bf16 path: workgroups of the step (the items list)
+  int32_t num_splits;        // bf16 path: split row groups
+  // bf16 path: partial merges of the split halves, [split][half][2 + DP / 2][256] floats
+  // (m, l, then the accumulator registers, of thread t of the workgroup at [.][t])
+  float* split_ws;
   int32_t num_slots;
   int32_t slot_rows;
   int32_t kt_pad;            // padded token count of the transposed-V scratch
@@ -104,6 +122,8 @@ struct StepArgs {
 
 hipError_t launch_zero_counters(unsigned long long* counters, int n, hipStream_t s);
 hipError_t launch_transpose_v(const StepArgs& a, hipStream_t s);
+// Both passes of the bf16 step, each followed by merge_splits when the plan has split row
+// groups.
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t s);
 // Planner reductions, on a plan whose row lists hold every active block of each row:

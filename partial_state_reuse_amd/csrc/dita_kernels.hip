@@ -11,8 +11,9 @@
 //   transpose_v     V [B,H,N,D] bf16 -> V^T scratch [B*H][DP][kt_pad] fp16, each partition's
 //                   key range padded with zeros to a multiple of the key tile.
 //   step_bf16<DP, MEASURE, FP8, FIXED>
-//                   one workgroup (4 waves) per (b, h, query partition i, row tile), or per
-//                   tail sub-tile.  For each fresh j: flash-attention over j's keys with MFMA
+//                   one workgroup (4 waves) per (b, h, query partition i, row tile), per
+//                   pack of tail sub-tiles, or per half of a split row tile (the plan's list
+//                   of workgroups).  For each fresh j: flash-attention over j's keys with MFMA
 //                   (S^T = K Q^T in bf16, then O^T += V^T P^T in fp16), K and V^T tiles
 //                   staged through LDS; at the block's end the normalised state goes to the
 //                   cache (bf16 or fp8 O, f32 lse) and is folded into the row's running
@@ -22,6 +23,8 @@
 //                   change, for steps that take no snapshot of them (otherwise diag_change
 //                   measures after the step); FIXED is the fixed-reference pass (below),
 //                   after which the FIXED = false kernel runs as a conditional second pass.
+//   merge_splits    after each pass: the two halves' partial merges of each split row tile
+//                   combined, and its rows written.
 //   step_f32        the same computation in plain fp32 VALU arithmetic, one lane per row.
 //   snapshot_diag   the diagonal slots copied aside before a measuring bf16 step.
 //   diag_change     after it, the diagonal states' squared change against that copy.
@@ -420,31 +423,25 @@ __device__ __forceinline__ void finish_rows(const StepArgs& a, int bh, int o_i, 
   }
 }
 
-// Reused blocks folded into the row's merge, then the epilogue.
-template <int DP, bool FP8>
-__device__ __forceinline__ void reuse_and_finish(const StepArgs& a, int bh, int i, int o_i,
-                                                 int n_i, int row0, int e0, int nf, int nr,
-                                                 f32x16 (&acc)[DP / 32], float m_row,
-                                                 float l_row) {
-  reuse_fold<DP, FP8, 1>(a, bh, row0, e0, nf, nf + nr, acc, m_row, l_row);
-  finish_rows<DP>(a, bh, o_i, n_i, row0, nf, nr, acc, m_row, l_row);
-}
-
 // Tail workgroup k: a pack of tail sub-tiles -- the rows left at the ends of consecutive
 // partitions, at most 32 in all -- whose lane l holds row r_l of partition i_l (its member's
 // rows follow one another over the lanes; lanes past the pack's rows hold none).  The 4
-// waves split the union of the members' fresh blocks (wave w takes every 4th from the w-th):
-// a wave computes its blocks over all 32 rows, and a lane keeps a block only where it is fresh
-// for its own partition, storing the state to that block's slot and folding it into its row's
-// partial merge.  Reused states are split alike (entry e of each row's reuse list for e = w,
-// w + 4, ...), every lane reading its own partition's slot.  K / V^T fragments come straight
-// from global memory (L2); the partial merges are combined through LDS (exact in any order)
-// and wave 0 writes the rows.  `lds` holds at least 2 x 64 x (2 + DP / 2) floats.
+// waves go through the union of the members' fresh blocks together, splitting each block's
+// keys (wave w takes every 4th 32-key unit from the w-th), over all 32 rows; the four
+// partial states of a block are merged exactly (any order) through LDS by wave 0, and a lane
+// keeps the block only where it is fresh for its own partition, storing the state to that
+// block's slot and folding it into its row's merge.  Reused states are split over the waves
+// (entry e of each row's reuse list for e = w, w + 4, ...), every lane reading its own
+// partition's slot.  K / V^T fragments come straight from global memory (L2); the partial
+// merges are combined through LDS (exact in any order) and wave 0 writes the rows.  `lds`
+// holds 4 slots of 64 x (2 + DP / 2) floats.
 template <int DP, bool MEASURE, bool FP8>
 __device__ __forceinline__ void tail_pack(const StepArgs& a, int bh, int k, float* lds) {
   constexpr int NKC = DP / 16, NDT = DP / 32;
   typedef typename CacheElem<FP8>::type CT;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index as a scalar, so that LDS addresses split into a scalar base and a per-lane
+  // offset with the element index as an immediate
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
   const cint* plan = as_const(a.plan);
   const cint* offs = plan + a.off_offs;
@@ -490,43 +487,62 @@ __device__ __forceinline__ void tail_pack(const StepArgs& a, int bh, int k, floa
       qf[kc] = as_bf16x8(v);
     }
   }
-  f32x16 acc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x16){};
+  // the row's merge: m, l in registers; during the fresh blocks wave 0 keeps O in LDS (in the
+  // slot of partial states that it does not use, 16 NDT floats per lane), which leaves the
+  // block loop the registers of its one-unit-ahead fragment loads
   float m_row = kNegInf, l_row = 0.f;
+  float* racc = lds + lane;                      // slot 0 (wave 0 leaves no partial state)
+  if (wave == 0) {
+#pragma unroll
+    for (int x = 0; x < NDT * 16; ++x) racc[x * 64] = 0.f;
+  }
   const size_t slot_elems = (size_t)a.slot_rows * DP;
   CT* cache_o = (CT*)a.cache_o;
   const uint16_t* Kg = (const uint16_t*)a.k + head_base(a, bh);
   const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
 
-  // ---------------- fresh blocks: the union of the members' ----------------
-  for (int t = wave; t < nu; t += kWaves) {
+  // ---------------- fresh blocks: the union of the members', one at a time ----------------
+  // Wave w takes the 32-key units w, w + 4, ... of the block, each unit's K and V^T fragments
+  // loaded one unit ahead (K after this unit's QK MFMAs, V^T after its PV MFMAs).  At the
+  // block's end waves 1-3 leave their partial states in LDS and wave 0 merges them into its
+  // own, then writes the block's state and folds it into the row's merge; waves 1-3 go on
+  // with the next block meanwhile.
+  constexpr int W = 2 + NDT * 16;               // floats per lane of a partial state
+  for (int t = 0; t < nu; ++t) {
     const int j = uent[2 * (u0 + t)], sb = uent[2 * (u0 + t) + 1];
-    const int slot = valid ? pslot[sb + mem] : -1;
-    const bool mine = slot >= 0;                 // j is fresh for this lane's partition
     const int o_j = offs[j], n_j = offs[j + 1] - o_j, po_j = poffs[j];
+    const int nunits = (n_j + 31) >> 5;
     f32x16 bacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) bacc[dt] = (f32x16){};
     float m_b = kNegInf, l_b = 0.f, thr = kNegInf;
-    for (int kbase = 0; kbase < n_j; kbase += 32) {
-      bf16x8 kf[NKC];
-      {
-        const int key = min(kbase + key_of_row(l32), n_j - 1);
-        const uint16_t* src = Kg + (size_t)(o_j + key) * a.ld;
+    bf16x8 kf[NKC];
+    f16x8 vf[NDT][2];
+    auto load_k = [&](int u) {
+      const int key = min(u * 32 + key_of_row(l32), n_j - 1);
+      const uint16_t* src = Kg + (size_t)(o_j + key) * a.ld;
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) kf[kc] = as_bf16x8(ld16(src + min(kc * 16 + h32 * 8, a.D - 8)));
-      }
-      f32x16 s = (f32x16){};
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], s, 0, 0, 0);
-      f16x8 vf[NDT][2];
+      for (int kc = 0; kc < NKC; ++kc) kf[kc] = as_bf16x8(ld16(src + min(kc * 16 + h32 * 8, a.D - 8)));
+    };
+    auto load_v = [&](int u) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          vf[dt][c] = as_f16x8(ld16(VTg + (size_t)(dt * 32 + l32) * a.kt_pad + po_j + kbase + c * 16 + h32 * 8));
+          vf[dt][c] = as_f16x8(ld16(VTg + (size_t)(dt * 32 + l32) * a.kt_pad + po_j + u * 32 + c * 16 + h32 * 8));
+    };
+    if (wave < nunits) {
+      load_k(wave);
+      load_v(wave);
+    }
+    for (int u = wave; u < nunits; u += kWaves) {
+      const int kbase = u * 32;
+      f32x16 s = (f32x16){};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], s, 0, 0, 0);
+      const bool more = u + kWaves < nunits;    // wave-uniform
+      if (more) load_k(u + kWaves);
       if (kbase + 32 > n_j) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
@@ -537,15 +553,18 @@ __device__ __forceinline__ void tail_pack(const StepArgs& a, int bh, int k, floa
       float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
       for (int q = 3; q < 16; q += 2) mx = fmaxf(fmaxf(mx, s[q]), s[q + 1 < 16 ? q + 1 : q]);
+      // the rescale factor is applied on every unit (1 without a new maximum): a rescale
+      // under a branch would keep two copies of the block accumulator live across it
+      float alpha = 1.f;
       if (__any(mx > thr)) {
         const float m_new = fmaxf(m_b, max_halves(mx, paddr) * sc);
-        const float alpha = fast_exp2(m_b - m_new);
+        alpha = fast_exp2(m_b - m_new);
         m_b = m_new;
         thr = (m_new + kRescaleSlack) * inv_sc;
-        l_b *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= alpha;
       }
+      l_b *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= alpha;
       f16x8 pf[2];
 #pragma unroll
       for (int q = 0; q < 16; ++q)
@@ -562,7 +581,48 @@ __device__ __forceinline__ void tail_pack(const StepArgs& a, int bh, int k, floa
 #pragma unroll
         for (int c = 0; c < 2; ++c)
           bacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[dt][c], pf[c], bacc[dt], 0, 0, 0);
+      if (more) load_v(u + kWaves);
     }
+    // the four partial states of the block, merged by wave 0 (a wave without keys holds
+    // m = -inf, l = 0, O = 0, which the merge weights by 0)
+    __syncthreads();                             // wave 0 has read the previous block's
+    if (wave != 0) {
+      float* p = lds + (size_t)wave * W * 64 + lane;
+      p[0] = m_b;
+      p[64] = l_b;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) p[(2 + dt * 16 + x) * 64] = bacc[dt][x];
+    }
+    __syncthreads();
+    if (wave != 0) continue;
+    {
+      float mw[kWaves - 1];
+      float mn = m_b;
+#pragma unroll
+      for (int w = 0; w < kWaves - 1; ++w) {
+        mw[w] = lds[(size_t)(w + 1) * W * 64 + lane];
+        mn = fmaxf(mn, mw[w]);
+      }
+      const float f0 = m_b == kNegInf ? 0.f : fast_exp2(m_b - mn);
+      l_b *= f0;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) bacc[dt] *= f0;
+#pragma unroll
+      for (int w = 0; w < kWaves - 1; ++w) {
+        const float* p = lds + (size_t)(w + 1) * W * 64 + lane;
+        const float fw = mw[w] == kNegInf ? 0.f : fast_exp2(mw[w] - mn);
+        l_b = __builtin_fmaf(p[64], fw, l_b);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) bacc[dt][x] = __builtin_fmaf(p[(2 + dt * 16 + x) * 64], fw, bacc[dt][x]);
+      }
+      m_b = mn;
+    }
+    const int slot = valid ? pslot[sb + mem] : -1;
+    const bool mine = slot >= 0;                 // j is fresh for this lane's partition
     // block end, for the lanes whose partition has j fresh: the normalised state to the slot
     // (fragment order, at this lane's row), the lse, and the fold into the row's merge
     const float lsum = sum_halves(l_b, paddr);
@@ -631,11 +691,21 @@ __device__ __forceinline__ void tail_pack(const StepArgs& a, int bh, int k, floa
       const float mn = fmaxf(m_row, lse2);
       const float fa = fast_exp2(m_row - mn), fb = fast_exp2(lse2 - mn);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * fa + bacc[dt] * fb;
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+          racc[(dt * 16 + x) * 64] = racc[(dt * 16 + x) * 64] * fa + bacc[dt][x] * fb;
       l_row = l_row * fa + fb;
       m_row = mn;
     }
   }
+
+  __syncthreads();                               // wave 0 has read the last block's partials
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) acc[dt][x] = wave == 0 ? racc[(dt * 16 + x) * 64] : 0.f;
 
   // ---------------- reused states: entry e of each row's list, e = wave, wave + 4, ... ----
   {
@@ -691,8 +761,8 @@ __device__ __forceinline__ void tail_pack(const StepArgs& a, int bh, int k, floa
     }
   }
 
-  // combine the partial merges: waves 2, 3 into 0, 1, then 1 into 0
-  constexpr int W = 2 + NDT * 16;               // floats per lane
+  // combine the partial merges: waves 2, 3 into 0, 1, then 1 into 0 (slot s of LDS holds the
+  // merge of wave s)
   auto put = [&](int sl) {
     float* p = lds + (size_t)sl * W * 64 + lane;
     p[0] = m_row;
@@ -715,14 +785,14 @@ __device__ __forceinline__ void tail_pack(const StepArgs& a, int bh, int k, floa
     l_row = l_row * fa + l2 * fb;
     m_row = mn;
   };
-  if (wave >= 2) put(wave - 2);
+  if (wave >= 2) put(wave);
   __syncthreads();
-  if (wave < 2) take(wave);
+  if (wave < 2) take(wave + 2);
   __syncthreads();
-  if (wave == 1) put(0);
+  if (wave == 1) put(1);
   __syncthreads();
   if (wave != 0) return;
-  take(0);
+  take(1);
   if (valid) {
     const float inv = 1.0f / l_row;
     const size_t orow = head_base(a, bh) + (size_t)(o_i + r) * a.ld;   // element offset
@@ -778,11 +848,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   constexpr int CHK = KT * DP / 8 / 256;   // 16-byte chunks per thread per K tile
   constexpr int CHV = DP * KT / 8 / 256;   // ... per V^T tile
   constexpr int WG_ROWS = kWaves * 32;
-  // K tile, then V^T tile; the tail workgroups use the same memory for their merge
-  __shared__ __attribute__((aligned(16))) uint16_t smem[KT * LDK + DP * LDV];
+  // K tile, then V^T tile; the tail workgroups use the same memory for one slot of 2 + DP / 2
+  // floats per lane and wave (partial states and merges)
+  constexpr int TILE_ELEMS = KT * LDK + DP * LDV;
+  constexpr int MERGE_ELEMS = kWaves * (2 + DP / 2) * 64 * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[TILE_ELEMS > MERGE_ELEMS ? TILE_ELEMS : MERGE_ELEMS];
   uint16_t* const sK = smem;
   uint16_t* const sV = smem + KT * LDK;
-  static_assert(sizeof(smem) >= 2 * 64 * (2 + DP / 2) * sizeof(float), "tail merge buffer");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h32 = lane >> 5, l32 = lane & 31;
@@ -791,14 +863,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     if (blockIdx.x == 0 && tid == 0) atomicAdd(&a.counters[3], 1ull);
   }
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = wg / a.num_tiles, tix = wg - bh * a.num_tiles;
   const cint* plan = as_const(a.plan);
   const cint* offs = plan + a.off_offs;
   const cint* poffs = plan + a.off_poffs;
-  const int packed = plan[a.off_tiles + tix];
+  const int bh = plan[a.off_items + 2 * wg];
+  int packed = plan[a.off_items + 2 * wg + 1];
   if (packed & kTailFlag) {                     // workgroup-uniform
     tail_pack<DP, MEASURE, FP8>(a, bh, packed & 0xffff, (float*)smem);
     return;
+  }
+  // half `half` of split row group `split` (-1: a whole row group)
+  int split = -1, half = 0;
+  if (packed & kSplitFlag) {
+    split = (packed & ~kSplitFlag) >> 1;
+    half = packed & 1;
+    packed = plan[a.off_splits + 2 * split + 1];
   }
   const int i = packed >> 16, t = packed & 0xffff;
   const int o_i = offs[i], n_i = offs[i + 1] - o_i;
@@ -807,6 +886,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const int myrow = row0 + l32;
   const cint* rinfo = plan + a.off_rows + 4 * i;
   const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
+  // this workgroup's share of the row's fresh blocks [f_lo, f_hi) and reused states
+  // [r_lo, r_hi): all of them, or for the halves of a split group the first ceil(nf / 2)
+  // fresh and floor(nr / 2) reused, and the rest
+  const int f_mid = (nf + 1) >> 1, r_mid = nr >> 1;
+  const int f_lo = split < 0 || half == 0 ? 0 : f_mid;
+  const int f_hi = split < 0 || half == 1 ? nf : f_mid;
+  const int r_lo = split < 0 || half == 0 ? 0 : r_mid;
+  const int r_hi = split < 0 || half == 1 ? nr : r_mid;
   const cint* ent = plan + a.off_ent;
   const float sc = a.scale_log2;
   const float inv_sc = 1.0f / sc;
@@ -839,7 +926,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
 
   // ---------------- fresh blocks ----------------
-  for (int e = 0; e < nf; ++e) {
+  for (int e = f_lo; e < f_hi; ++e) {
     const int j = ent[2 * (e0 + e)], slot = ent[2 * (e0 + e) + 1];
     const int o_j = offs[j], n_j = offs[j + 1] - o_j, po_j = poffs[j];
     const int ntile = (n_j + KT - 1) / KT;
@@ -957,7 +1044,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   }
   if (!live) return;
 
-  reuse_and_finish<DP, FP8>(a, bh, i, o_i, n_i, row0, e0, nf, nr, acc, m_row, l_row);
+  reuse_fold<DP, FP8, 1>(a, bh, row0, e0, nf + r_lo, nf + r_hi, acc, m_row, l_row);
+  if (split < 0) {
+    finish_rows<DP>(a, bh, o_i, n_i, row0, nf, nr, acc, m_row, l_row);
+    return;
+  }
+  // a split half: the partial merge of its rows to the workspace, for merge_splits
+  float* ws = a.split_ws + (size_t)(2 * split + half) * (2 + NDT * 16) * 256 + tid;
+  ws[0] = m_row;
+  ws[256] = l_row;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) ws[(2 + dt * 16 + x) * 256] = acc[dt][x];
+}
+
+// The two halves of each split row group merged (DiTango, "State-Centric Parallel Runtime /
+// Composizione dello Stato": partial attention states combine through their log-sum-exp in
+// any grouping; here as two partial merges of the rows:
+// the first half's weighted by 2^(m1 - m), the second's by 2^(m2 - m), m the larger, the
+// same arithmetic whichever half finished first), then the rows written as finish_rows does
+// for a whole group.  One workgroup of 256 threads per split group; thread t takes the
+// values thread t of the step's workgroup left.  In the conditional second pass it runs
+// only if the first pass rejected a reference.
+template <int DP>
+__global__ __launch_bounds__(256) void merge_splits(StepArgs a) {
+  constexpr int NDT = DP / 32;
+  constexpr int W = 2 + NDT * 16;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  if (a.fixup && a.counters[4] == 0) return;
+  const int s = blockIdx.x;
+  const cint* plan = as_const(a.plan);
+  const int bh = plan[a.off_splits + 2 * s], packed = plan[a.off_splits + 2 * s + 1];
+  const int i = packed >> 16, t = packed & 0xffff;
+  const cint* offs = plan + a.off_offs;
+  const int o_i = offs[i], n_i = offs[i + 1] - o_i;
+  const int row0 = t * kWaves * 32 + wave * 32;
+  if (row0 >= n_i) return;                      // wave-uniform: no rows here
+  const cint* rinfo = plan + a.off_rows + 4 * i;
+  const float* w1 = a.split_ws + (size_t)s * 2 * W * 256 + tid;
+  const float* w2 = w1 + (size_t)W * 256;
+  const float m1 = w1[0], m2 = w2[0];
+  const float m = fmaxf(m1, m2);
+  const float f1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - m);
+  const float f2 = m2 == kNegInf ? 0.f : fast_exp2(m2 - m);
+  const float l = w1[256] * f1 + w2[256] * f2;
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int x = 0; x < 16; ++x)
+      acc[dt][x] = w1[(2 + dt * 16 + x) * 256] * f1 + w2[(2 + dt * 16 + x) * 256] * f2;
+  finish_rows<DP>(a, bh, o_i, n_i, row0, rinfo[1], rinfo[2], acc, m, l);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1456,13 +1594,15 @@ hipError_t launch_transpose_v(const StepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_step_bf16(const StepArgs& args, hipStream_t s) {
-  const int G = args.num_tiles * args.B * args.H;
+  const int G = args.num_items;
   StepArgs a = args;
   a.fixup = 0;
   // a measuring step takes the fixed-reference pass only with the snapshot of the old diagonal
   // states (a second pass would otherwise measure against the first pass's writes)
   const int m = a.delta_part != nullptr ? 1 : 0, f = a.cache_fp8 ? 2 : 0;
   const bool fixed = a.fixed_ref && (!m || a.diag_snap);
+#define DITA_MERGE_SPLITS(DPV)                                                                   \
+  if (a.num_splits > 0) hipLaunchKernelGGL((merge_splits<DPV>), dim3(a.num_splits), dim3(256), 0, s, a);
 #define DITA_LAUNCH_BF16(DPV)                                                                    \
   if (fixed) {                                                                                   \
     switch (m | f) {                                                                             \
@@ -1471,6 +1611,7 @@ hipError_t launch_step_bf16(const StepArgs& args, hipStream_t s) {
       case 2: hipLaunchKernelGGL((step_bf16<DPV, false, true, true>), dim3(G), dim3(256), 0, s, a); break;  \
       default: hipLaunchKernelGGL((step_bf16<DPV, true, true, true>), dim3(G), dim3(256), 0, s, a); break;  \
     }                                                                                            \
+    DITA_MERGE_SPLITS(DPV)                                                                       \
     a.fixup = 1;                                                                                 \
   }                                                                                              \
   switch (m | f) {                                                                               \
@@ -1478,7 +1619,8 @@ hipError_t launch_step_bf16(const StepArgs& args, hipStream_t s) {
     case 1: hipLaunchKernelGGL((step_bf16<DPV, true, false, false>), dim3(G), dim3(256), 0, s, a); break;  \
     case 2: hipLaunchKernelGGL((step_bf16<DPV, false, true, false>), dim3(G), dim3(256), 0, s, a); break;  \
     default: hipLaunchKernelGGL((step_bf16<DPV, true, true, false>), dim3(G), dim3(256), 0, s, a); break;  \
-  }
+  }                                                                                              \
+  DITA_MERGE_SPLITS(DPV)
   switch (a.DP) {
     case 64: DITA_LAUNCH_BF16(64) break;
     case 96: DITA_LAUNCH_BF16(96) break;
@@ -1486,6 +1628,7 @@ hipError_t launch_step_bf16(const StepArgs& args, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 #undef DITA_LAUNCH_BF16
+#undef DITA_MERGE_SPLITS
   return hipGetLastError();
 }
 
