@@ -257,9 +257,10 @@ dita_status dita_get_block_plan(const dita_cache* cache, uint8_t* mask, int32_t*
  * combines, so the grid ends on short workgroups; their rows' sums are associated
  * differently, so outputs may differ in the last bits from a run without splits.  By
  * default an eighth of an XCD's concurrent workgroups are split when the step runs two
- * rounds of workgroups or more; the environment variable DITA_SPLITS_PER_XCD, read when a
- * geometry is resolved (by dita_cache_required_bytes and dita_cache_alloc), sets the number
- * of split row groups per XCD instead (0: none; at most 128).
+ * rounds of workgroups or more.  Environment variables read when a geometry is resolved
+ * (by dita_cache_required_bytes and dita_cache_alloc) override this: DITA_SPLITS_PER_XCD
+ * sets the number of split row groups per XCD (0: none; at most 128), DITA_SPLIT_PARTS the
+ * workgroups per split group (2 to 8).
  * Errors: INVALID_ARGUMENT, NO_POLICY, DEVICE. */
 dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, const void* v,
                            void* out, float* lse_out, void* hip_stream);
@@ -279,8 +280,8 @@ dita_status dita_attn_step(dita_cache* cache, const void* q, const void* k, cons
  *   - Not profiled (dita_set_profiling does not time it).
  * Errors: those of dita_attn_step, and UNSUPPORTED when the step's scratch (B*H*DP*kt_pad*2
  * bytes of transposed V, DP the padded head dim and kt_pad the token count with each
- * partition padded to 64, plus the work lists and 2 x 256 x (2 + DP/2) x 4 bytes per split
- * row group) exceeds 128 MiB, or when the pending policy
+ * partition padded to 64, plus the work lists and parts x 256 x (2 + DP/2) x 4 bytes per
+ * split row group) exceeds 128 MiB, or when the pending policy
  * is a PLANNER step (its measurements are read back into host memory of the library's own). */
 dita_status dita_attn_step_static(dita_cache* cache, const void* q, const void* k,
                                   const void* v, void* out, float* lse_out, void* hip_stream);

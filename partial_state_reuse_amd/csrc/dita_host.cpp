@@ -66,7 +66,7 @@ struct Geo {
   // split row groups {b*H + h, tile word of the group}
   std::vector<int32_t> items;
   std::vector<int32_t> splits;
-  int num_items = 0, num_splits = 0;
+  int num_items = 0, num_splits = 0, split_parts = 2;
   int slot_rows = 0;
   bool bf16() const { return qkv == DITA_BF16; }
   // bytes per cached O element
@@ -76,13 +76,14 @@ struct Geo {
 // The bf16 step's workgroups in logical order.  Workgroup ids are dealt round-robin to the 8
 // XCDs and the kernel maps XCD x's ids onto the x-th contiguous range of logical indices
 // (xcd_remap), so XCD x runs its range front to back.  The (b, h) tiles are laid out head
-// after head; in each XCD's range the last K row groups are split in two halves, which
-// become adjacent workgroups of about half the length, so that the grid's end on that XCD
-// is made of short workgroups.  K is an eighth of the XCD's concurrent workgroups (32 CUs
-// x 3 at DP = 64, x 2 above), and 0 when the range holds fewer than two rounds of them or
-// when some range has fewer than K row groups (not tail workgroups) to split.  The
-// environment variable DITA_SPLITS_PER_XCD, read when a geometry is resolved, sets K
-// instead (0 turns the splitting off; at most kMaxSplits / 8).
+// after head; in each XCD's range the last K row groups are split in NP parts, which become
+// adjacent workgroups of about 1 / NP of the length, so that the grid's end on that XCD is
+// made of short workgroups.  K is an eighth of the XCD's concurrent workgroups (32 CUs x 3 at
+// DP = 64, x 2 above), and 0 when the range holds fewer than two rounds of them or when some
+// range has fewer than K row groups (not tail workgroups) to split.  The environment
+// variables DITA_SPLITS_PER_XCD (0 turns the splitting off; at most kMaxSplits / 8) and
+// DITA_SPLIT_PARTS (2 to kMaxSplitParts), read when a geometry is resolved, set K and NP.
+constexpr int kDefaultSplitParts = 2;
 void build_items(Geo* r) {
   const int64_t G0 = (int64_t)r->B * r->H * r->num_tiles;
   std::vector<int32_t> word(r->num_tiles);   // tile words of one (b, h), in order
@@ -97,8 +98,12 @@ void build_items(Geo* r) {
   int K = G0 / 8 >= 2 * slots ? slots / 8 : 0;
   if (const char* e = std::getenv("DITA_SPLITS_PER_XCD")) K = std::max(0, std::atoi(e));
   K = std::min(K, dita::kMaxSplits / 8);
+  int NP = kDefaultSplitParts;
+  if (const char* e = std::getenv("DITA_SPLIT_PARTS"))
+    NP = std::max(2, std::min(dita::kMaxSplitParts, std::atoi(e)));
+  r->split_parts = NP;
   for (;; K = 0) {
-    const int64_t G = G0 + 8 * (int64_t)K;
+    const int64_t G = G0 + 8 * (int64_t)K * (NP - 1);
     r->items.clear();
     r->splits.clear();
     r->items.reserve(2 * G);
@@ -106,7 +111,7 @@ void build_items(Geo* r) {
     bool short_of_groups = false;
     for (int x = 0; x < 8 && !short_of_groups; ++x) {
       const int64_t chunk = G / 8 + (x < G % 8 ? 1 : 0);
-      const int64_t n = chunk - K;    // regular tiles of this XCD's range
+      const int64_t n = chunk - (int64_t)K * (NP - 1);   // regular tiles of this XCD's range
       std::vector<uint8_t> split_here(n, 0);
       int need = K;
       for (int64_t y = n - 1; y >= 0 && need > 0; --y)
@@ -129,9 +134,9 @@ void build_items(Geo* r) {
         const int sidx = (int)(r->splits.size() / 2);
         r->splits.push_back(bh);
         r->splits.push_back(w);
-        for (int half = 0; half < 2; ++half) {
+        for (int part = 0; part < NP; ++part) {
           r->items.push_back(bh);
-          r->items.push_back(dita::kSplitFlag | (sidx << 1) | half);
+          r->items.push_back(dita::kSplitFlag | (sidx << 3) | part);
         }
       }
       cursor += n;
@@ -476,9 +481,9 @@ struct Layout {
          wpart = 0, merge = 0, merge_bytes = 0, snap = 0, split_ws = 0, total = 0;
 };
 
-// Bytes of the split halves' partial merges: per half, 256 threads x (m, l, DP / 2 values).
+// Bytes of the split parts' partial merges: per part, 256 threads x (m, l, DP / 2 values).
 size_t split_ws_bytes(const Geo& g) {
-  return (size_t)g.num_splits * 2 * 256 * (2 + g.DP / 2) * 4;
+  return (size_t)g.num_splits * g.split_parts * 256 * (2 + g.DP / 2) * 4;
 }
 
 // The persistent part of the device buffer, as offloaded to the host: the counters, then
@@ -744,6 +749,7 @@ void fill_args(const dita_cache* c, int plan_slot, dita::StepArgs* a) {
   a->off_splits = a->off_items + (int32_t)g.items.size();
   a->num_items = g.num_items;
   a->num_splits = g.num_splits;
+  a->split_parts = g.split_parts;
   a->split_ws = (float*)(c->dev + c->L.split_ws);
   a->B = g.B; a->H = g.H; a->N = g.N; a->D = g.D; a->DP = g.DP; a->P = P;
   if (g.layout == DITA_LAYOUT_BNHD) {

@@ -51,18 +51,20 @@ inline int bf16_wg_rows(int /*DP*/) { return kWaves * 32; }
 //   items  at pslot + P * members         : bf16 path: 2 words per workgroup {b*H + h, tile
 //                                           word}, in the order of the logical workgroup index
 //                                           (after the XCD remap); the tile word is a group or
-//                                           tail word as above, or kSplitFlag | (s << 1) | half
-//                                           for half of split row group s
+//                                           tail word as above, or kSplitFlag | (s << 3) | part
+//                                           for part `part` of split row group s
 //   splits at items + 2 * items           : 2 words per split row group {b*H + h, group word}
 constexpr int kPlanHeader = 4;
 constexpr int32_t kTailFlag = 1 << 30;
-// bf16 path: the row groups dispatched last on each XCD run as two workgroups each (the
-// first and second half of the row's fresh blocks and of its reused states), so that the
-// grid ends on workgroups of half the length; each half leaves its partial merge of the rows
-// in a workspace and merge_splits combines the two and writes the rows.
+// bf16 path: the row groups dispatched last on each XCD run as split_parts workgroups each
+// (consecutive shares of the row's fresh blocks and of its reused states), so that the grid
+// ends on short workgroups; each part leaves its partial merge of the rows in a workspace and
+// merge_splits combines the parts and writes the rows.
 constexpr int32_t kSplitFlag = 1 << 29;
 // at most this many split row groups per step
 constexpr int kMaxSplits = 1024;
+// at most this many parts per split row group
+constexpr int kMaxSplitParts = 8;
 // bf16 path: a partition whose last row group would leave at most this many of its 4 waves
 // with rows hands those rows to tail sub-tiles instead; the tail sub-tiles of consecutive
 // partitions are packed into 32-row tiles while their rows fit, one workgroup per pack, whose
@@ -95,7 +97,8 @@ struct StepArgs {
   int32_t num_tiles;         // workgroup tiles per (b, h)
   int32_t num_items;         // bf16 path: workgroups of the step (the items list)
   int32_t num_splits;        // bf16 path: split row groups
-  // bf16 path: partial merges of the split halves, [split][half][2 + DP / 2][256] floats
+  int32_t split_parts;       // bf16 path: workgroups per split row group
+  // bf16 path: partial merges of the split parts, [split][part][2 + DP / 2][256] floats
   // (m, l, then the accumulator registers, of thread t of the workgroup at [.][t])
   float* split_ws;
   int32_t num_slots;

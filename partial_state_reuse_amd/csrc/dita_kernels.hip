@@ -12,7 +12,7 @@
 //                   key range padded with zeros to a multiple of the key tile.
 //   step_bf16<DP, MEASURE, FP8, FIXED>
 //                   one workgroup (4 waves) per (b, h, query partition i, row tile), per
-//                   pack of tail sub-tiles, or per half of a split row tile (the plan's list
+//                   pack of tail sub-tiles, or per part of a split row tile (the plan's list
 //                   of workgroups).  For each fresh j: flash-attention over j's keys with MFMA
 //                   (S^T = K Q^T in bf16, then O^T += V^T P^T in fp16), K and V^T tiles
 //                   staged through LDS; at the block's end the normalised state goes to the
@@ -23,7 +23,7 @@
 //                   change, for steps that take no snapshot of them (otherwise diag_change
 //                   measures after the step); FIXED is the fixed-reference pass (below),
 //                   after which the FIXED = false kernel runs as a conditional second pass.
-//   merge_splits    after each pass: the two halves' partial merges of each split row tile
+//   merge_splits    after each pass: the parts' partial merges of each split row tile
 //                   combined, and its rows written.
 //   step_f32        the same computation in plain fp32 VALU arithmetic, one lane per row.
 //   snapshot_diag   the diagonal slots copied aside before a measuring bf16 step.
@@ -872,11 +872,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     tail_pack<DP, MEASURE, FP8>(a, bh, packed & 0xffff, (float*)smem);
     return;
   }
-  // half `half` of split row group `split` (-1: a whole row group)
-  int split = -1, half = 0;
+  // part `part` of split row group `split` (-1: a whole row group)
+  int split = -1, part = 0;
   if (packed & kSplitFlag) {
-    split = (packed & ~kSplitFlag) >> 1;
-    half = packed & 1;
+    split = (packed & ~kSplitFlag) >> 3;
+    part = packed & 7;
     packed = plan[a.off_splits + 2 * split + 1];
   }
   const int i = packed >> 16, t = packed & 0xffff;
@@ -887,13 +887,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const cint* rinfo = plan + a.off_rows + 4 * i;
   const int e0 = rinfo[0], nf = rinfo[1], nr = rinfo[2];
   // this workgroup's share of the row's fresh blocks [f_lo, f_hi) and reused states
-  // [r_lo, r_hi): all of them, or for the halves of a split group the first ceil(nf / 2)
-  // fresh and floor(nr / 2) reused, and the rest
-  const int f_mid = (nf + 1) >> 1, r_mid = nr >> 1;
-  const int f_lo = split < 0 || half == 0 ? 0 : f_mid;
-  const int f_hi = split < 0 || half == 1 ? nf : f_mid;
-  const int r_lo = split < 0 || half == 0 ? 0 : r_mid;
-  const int r_hi = split < 0 || half == 1 ? nr : r_mid;
+  // [r_lo, r_hi): all of them, or for part p of a split group of np parts the p-th of np
+  // consecutive shares of each list ([p n / np, (p + 1) n / np))
+  const int np = split < 0 ? 1 : a.split_parts;
+  const int f_lo = part * nf / np, f_hi = (part + 1) * nf / np;
+  const int r_lo = part * nr / np, r_hi = (part + 1) * nr / np;
   const cint* ent = plan + a.off_ent;
   const float sc = a.scale_log2;
   const float inv_sc = 1.0f / sc;
@@ -1049,8 +1047,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     finish_rows<DP>(a, bh, o_i, n_i, row0, nf, nr, acc, m_row, l_row);
     return;
   }
-  // a split half: the partial merge of its rows to the workspace, for merge_splits
-  float* ws = a.split_ws + (size_t)(2 * split + half) * (2 + NDT * 16) * 256 + tid;
+  // a split part: the partial merge of its rows to the workspace, for merge_splits
+  float* ws = a.split_ws + (size_t)(split * a.split_parts + part) * (2 + NDT * 16) * 256 + tid;
   ws[0] = m_row;
   ws[256] = l_row;
 #pragma unroll
@@ -1059,14 +1057,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     for (int x = 0; x < 16; ++x) ws[(2 + dt * 16 + x) * 256] = acc[dt][x];
 }
 
-// The two halves of each split row group merged (DiTango, "State-Centric Parallel Runtime /
+// The parts of each split row group merged (DiTango, "State-Centric Parallel Runtime /
 // Composizione dello Stato": partial attention states combine through their log-sum-exp in
-// any grouping; here as two partial merges of the rows:
-// the first half's weighted by 2^(m1 - m), the second's by 2^(m2 - m), m the larger, the
-// same arithmetic whichever half finished first), then the rows written as finish_rows does
-// for a whole group.  One workgroup of 256 threads per split group; thread t takes the
-// values thread t of the step's workgroup left.  In the conditional second pass it runs
-// only if the first pass rejected a reference.
+// any grouping; here as partial merges of the rows: part p's weighted by 2^(m_p - m), m the
+// largest, summed in the order of the parts, whichever finished first), then the rows written
+// as finish_rows does for a whole group.  One workgroup of 256 threads per split group;
+// thread t takes the values thread t of each part's workgroup left.  In the conditional
+// second pass it runs only if the first pass rejected a reference.
 template <int DP>
 __global__ __launch_bounds__(256) void merge_splits(StepArgs a) {
   constexpr int NDT = DP / 32;
@@ -1082,19 +1079,25 @@ __global__ __launch_bounds__(256) void merge_splits(StepArgs a) {
   const int row0 = t * kWaves * 32 + wave * 32;
   if (row0 >= n_i) return;                      // wave-uniform: no rows here
   const cint* rinfo = plan + a.off_rows + 4 * i;
-  const float* w1 = a.split_ws + (size_t)s * 2 * W * 256 + tid;
-  const float* w2 = w1 + (size_t)W * 256;
-  const float m1 = w1[0], m2 = w2[0];
-  const float m = fmaxf(m1, m2);
-  const float f1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - m);
-  const float f2 = m2 == kNegInf ? 0.f : fast_exp2(m2 - m);
-  const float l = w1[256] * f1 + w2[256] * f2;
+  const int np = a.split_parts;
+  const float* w0 = a.split_ws + (size_t)s * np * W * 256 + tid;
+  float m = kNegInf;
+  for (int p = 0; p < np; ++p) m = fmaxf(m, w0[(size_t)p * W * 256]);
+  float l = 0.f;
   f32x16 acc[NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x16){};
+  for (int p = 0; p < np; ++p) {
+    const float* w = w0 + (size_t)p * W * 256;
+    const float mp = w[0];
+    const float f = mp == kNegInf ? 0.f : fast_exp2(mp - m);
+    l = __builtin_fmaf(w[256], f, l);
 #pragma unroll
-    for (int x = 0; x < 16; ++x)
-      acc[dt][x] = w1[(2 + dt * 16 + x) * 256] * f1 + w2[(2 + dt * 16 + x) * 256] * f2;
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+        acc[dt][x] = __builtin_fmaf(w[(2 + dt * 16 + x) * 256], f, acc[dt][x]);
+  }
   finish_rows<DP>(a, bh, o_i, n_i, row0, rinfo[1], rinfo[2], acc, m, l);
 }
 

@@ -1,9 +1,9 @@
 // Host check of the bf16 step's workgroup list (build_items in dita_host.cpp, compiled into
 // this translation unit): every (b, h) tile appears exactly once, as one workgroup or as the
-// two adjacent halves of a split row group inside one XCD range; the kernel's hardware-to-
-// logical remap is a bijection on the list; every XCD range holds the same number of split
-// groups; and the split count follows its rule (an eighth of an XCD's concurrent workgroups
-// from two rounds on, none for smaller grids, DITA_SPLITS_PER_XCD when set).
+// adjacent parts of a split row group inside one XCD range; the kernel's hardware-to-logical
+// remap is a bijection on the list; every XCD range holds the same number of split groups;
+// and the split count follows its rule (an eighth of an XCD's concurrent workgroups from two
+// rounds on, none for smaller grids, DITA_SPLITS_PER_XCD and DITA_SPLIT_PARTS when set).
 // Exit status 0 when every case holds.
 #include "dita_host.cpp"
 
@@ -18,7 +18,8 @@ int xcd_remap_host(int bid, int G) {            // the kernel's xcd_remap
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
-int check(int B, int H, int frames, int gh, int gw, int P, int D, int want_per_xcd) {
+int check(int B, int H, int frames, int gh, int gw, int P, int D, int want_per_xcd,
+          int want_parts = 2) {
   dita_geometry g{};
   g.batch = B; g.heads = H; g.tokens = frames * gh * gw; g.head_dim = D;
   g.frames = frames; g.grid_h = gh; g.grid_w = gw; g.num_partitions = P;
@@ -32,28 +33,31 @@ int check(int B, int H, int frames, int gh, int gw, int P, int D, int want_per_x
   const long G0 = (long)B * H * r.num_tiles;
   const int G = r.num_items;
   int bad = 0;
-  if ((long)G != G0 + r.num_splits) bad |= 1;
+  const int NP = r.split_parts;
+  if (NP != want_parts) bad |= 512;
+  if ((long)G != G0 + (long)r.num_splits * (NP - 1)) bad |= 1;
   std::vector<int> seen(G, 0);
   for (int b = 0; b < G; ++b) {
     const int l = xcd_remap_host(b, G);
     if (l < 0 || l >= G || seen[l]++) bad |= 2;
   }
   std::map<std::pair<int, int>, int> cnt;
-  std::vector<int> halves(r.num_splits, 0);
+  std::vector<int> parts(r.num_splits, 0);
   for (int x = 0; x < G; ++x) {
     const int bh = r.items[2 * x], w = r.items[2 * x + 1];
     if (w & dita::kSplitFlag) {
-      const int s = (w & ~dita::kSplitFlag) >> 1, h = w & 1;
+      const int s = (w & ~dita::kSplitFlag) >> 3, h = w & 7;
       if (r.splits[2 * s] != bh) bad |= 4;
-      halves[s] |= 1 << h;
-      if (h == 1 && (x == 0 || r.items[2 * x - 1] != (dita::kSplitFlag | (s << 1)))) bad |= 8;
+      parts[s] |= 1 << h;
+      if (h > 0 && (x == 0 || r.items[2 * x - 1] != (dita::kSplitFlag | (s << 3) | (h - 1))))
+        bad |= 8;
       if (h == 0) cnt[{bh, r.splits[2 * s + 1]}]++;
     } else {
       cnt[{bh, w}]++;
     }
   }
   for (int s = 0; s < r.num_splits; ++s)
-    if (halves[s] != 3) bad |= 16;
+    if (parts[s] != (1 << NP) - 1) bad |= 16;
   for (int bh = 0; bh < B * H; ++bh) {
     for (int k = 0; k < r.num_tail_wg; ++k)
       if (cnt[{bh, dita::kTailFlag | k}] != 1) bad |= 32;
@@ -73,16 +77,16 @@ int check(int B, int H, int frames, int gh, int gw, int P, int D, int want_per_x
   int per_range[8] = {0};
   for (int x = 0; x < G; ++x) {
     const int w = r.items[2 * x + 1];
-    if ((w & dita::kSplitFlag) && (w & 1) == 0) {
-      if (range_of(x) != range_of(x + 1)) bad |= 128;
+    if ((w & dita::kSplitFlag) && (w & 7) == 0) {
+      if (range_of(x) != range_of(x + NP - 1)) bad |= 128;
       per_range[range_of(x)]++;
     }
   }
   for (int x = 0; x < 8; ++x)
     if (per_range[x] != want_per_xcd) bad |= 256;
-  printf("B%d H%d N%d P%d D%d: tiles/bh %d tails %d G0 %ld splits %d (%d per XCD, want %d) "
-         "-> %s (%d)\n", B, H, g.tokens, P, D, r.num_tiles, r.num_tail_wg, G0, r.num_splits,
-         per_range[0], want_per_xcd, bad ? "BAD" : "ok", bad);
+  printf("B%d H%d N%d P%d D%d: tiles/bh %d tails %d G0 %ld splits %d x %d parts (%d per XCD, "
+         "want %d) -> %s (%d)\n", B, H, g.tokens, P, D, r.num_tiles, r.num_tail_wg, G0,
+         r.num_splits, NP, per_range[0], want_per_xcd, bad ? "BAD" : "ok", bad);
   return bad ? 1 : 0;
 }
 
@@ -91,6 +95,7 @@ int check(int B, int H, int frames, int gh, int gw, int P, int D, int want_per_x
 int main() {
   int bad = 0;
   unsetenv("DITA_SPLITS_PER_XCD");
+  unsetenv("DITA_SPLIT_PARTS");
   bad += check(1, 24, 8, 45, 80, 32, 64, 12);    // 29 frames of 720p: 5472 workgroups
   bad += check(2, 40, 17, 26, 60, 16, 128, 8);   // CFG long video, D = 128
   bad += check(1, 24, 24, 45, 80, 24, 64, 12);   // 93 frames
@@ -108,5 +113,14 @@ int main() {
   bad += check(1, 24, 8, 45, 80, 32, 64, 0);
   setenv("DITA_SPLITS_PER_XCD", "1000", 1);
   bad += check(1, 24, 8, 45, 80, 32, 64, dita::kMaxSplits / 8);
+  unsetenv("DITA_SPLITS_PER_XCD");
+  setenv("DITA_SPLIT_PARTS", "4", 1);
+  bad += check(1, 24, 8, 45, 80, 32, 64, 12, 4);
+  bad += check(2, 40, 17, 26, 60, 16, 128, 8, 4);
+  setenv("DITA_SPLITS_PER_XCD", "2", 1);
+  setenv("DITA_SPLIT_PARTS", "3", 1);
+  bad += check(1, 3, 4, 20, 26, 8, 64, 2, 3);
+  setenv("DITA_SPLIT_PARTS", "99", 1);
+  bad += check(1, 3, 4, 20, 26, 8, 64, 2, dita::kMaxSplitParts);
   return bad ? 1 : 0;
 }

@@ -1,16 +1,15 @@
 """GPU: split row groups, through the C ABI.
 
-On the bf16 path the row groups dispatched last on each XCD run as two workgroups, the
-first and second half of the row's fresh blocks and reused states, each leaving its partial
-merge of the rows in a workspace, and merge_splits combines the two halves and writes the
-rows.  The merge is the same log-sum-exp merge as the one over blocks (DiTango, "State-Centric
+On the bf16 path the row groups dispatched last on each XCD run as two (or more) workgroups,
+consecutive shares of the row's fresh blocks and reused states, each leaving its partial
+merge of the rows in a workspace, and merge_splits combines the parts and writes the rows.  The merge is the same log-sum-exp merge as the one over blocks (DiTango, "State-Centric
 Parallel Runtime / Composizione dello Stato": attention states, output and log-sum-exp,
 combine associatively and commutatively), so a split run must meet the fp64 oracle's bars
 like any other, and agree with the unsplit run up to the association of the sums.
 
 The default splits only grids of two rounds of workgroups and more (the full-size parity
 tests run it); here DITA_SPLITS_PER_XCD forces splits on small workloads, whose every row
-is then compared: bf16 with tail workgroups, D = 128, a bf16 output, a
+is then compared: bf16 with tail workgroups (in 2 and in 3 parts), D = 128, a bf16 output, a
 fixed reference that is rejected (the second pass re-runs the splits), the allocation-free
 step, and the workspace's size in the cache's bytes.  With an fp8 cache the split run is
 held to the unsplit one (the fp8 cache's own bars are those of its tests)."""
@@ -43,9 +42,9 @@ def _cfg(name, idx, **kw):
     return custom_config(name=name, idx=idx, **d)
 
 
-def _split_bytes(cfg, splits):
+def _split_bytes(cfg, splits, parts=2):
     dp = 64 if cfg.head_dim <= 64 else (96 if cfg.head_dim <= 96 else 128)
-    return splits * 2 * 256 * (2 + dp // 2) * 4
+    return splits * parts * 256 * (2 + dp // 2) * 4
 
 
 def _required(dita, cfg):
@@ -56,12 +55,15 @@ def _required(dita, cfg):
     return n
 
 
-@pytest.mark.parametrize("case", ["bf16-d64-tails", "bf16-d128", "bf16-out"])
+@pytest.mark.parametrize("case", ["bf16-d64-tails", "bf16-d64-3-parts", "bf16-d128",
+                                  "bf16-out"])
 def test_forced_splits_meet_the_oracle(dita, monkeypatch, case):
     from test_gpu_parity import run_and_check
-    if case == "bf16-d64-tails":
+    parts = 3 if case == "bf16-d64-3-parts" else 2
+    monkeypatch.setenv("DITA_SPLIT_PARTS", str(parts))
+    if case.startswith("bf16-d64"):
         # 260-row partitions: two row groups and a 4-row tail each, 17 workgroups per head
-        cfg = _cfg("split-d64", 95)
+        cfg = _cfg("split-d64", 95, steps=3 if parts == 2 else 4)
     elif case == "bf16-d128":
         cfg = _cfg("split-d128", 96, heads=2, head_dim=128, grid_h=24, grid_w=24,
                    num_partitions=6)
@@ -71,11 +73,14 @@ def test_forced_splits_meet_the_oracle(dita, monkeypatch, case):
     plain = _required(dita, cfg)
     monkeypatch.setenv("DITA_SPLITS_PER_XCD", "2")
     split = _required(dita, cfg)
-    # 2 row groups split on each of the 8 XCD ranges: 16 pairs of partial merges, and the
-    # work lists of the 4 plan slots a few words longer
-    assert _split_bytes(cfg, 16) <= split - plain <= _split_bytes(cfg, 16) + 5 * 256, \
-        (split, plain)
-    log(f"case {cfg.name}: 16 split row groups, workspace {split - plain} bytes")
+    # 2 row groups split on each of the 8 XCD ranges: 16 sets of partial merges, and the
+    # work lists of the 4 plan slots longer by 2 words per added workgroup and per split
+    # group (each slot rounded up to 256 bytes)
+    want = _split_bytes(cfg, 16, parts)
+    plan_words = 2 * 16 * (parts - 1) + 2 * 16
+    slack = 4 * (-(-plan_words * 4 // 256) + 1) * 256
+    assert want <= split - plain <= want + slack, (split, plain)
+    log(f"case {cfg.name}: 16 row groups split in {parts}, workspace {split - plain} bytes")
     if case == "bf16-out":
         _bf16_out_against_f32(dita, monkeypatch, cfg)
         return
