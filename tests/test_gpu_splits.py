@@ -163,3 +163,51 @@ def test_rejected_reference_with_splits(dita, monkeypatch):
         for bh in kept:
             kept[bh][1][1][j0:j1] *= 4
     run_and_check(dita, cfg, heads=[(0, 0), (0, 1)], modify=modify, recomputes="some")
+
+
+def _split_sweep_case(seed, sub):
+    """A random workload meant to hold split row groups: 2-3 heads, 2-4 frames of a 16-24 x
+    20-30 grid, 2-8 partitions (a few row groups each, ragged tails), head dim 64, 72, 96 or
+    128, 2-4 steps and a random policy kind; with K in 1-3 split groups per XCD range and 2-4
+    parts."""
+    rng = np.random.default_rng(7000 + 100 * seed + sub)
+    T, gh_, gw = int(rng.integers(2, 5)), int(rng.integers(16, 25)), int(rng.integers(20, 31))
+    P = int(rng.integers(2, 9))
+    D = int(rng.choice([64, 72, 96, 128]))
+    H, S = int(rng.integers(2, 4)), int(rng.integers(2, 5))
+    N = T * gh_ * gw
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        pol = Policy(kind=wcfg.FRESH_BUDGET, reuse_percent=int(rng.integers(0, 101)))
+    elif kind == 1:
+        pol = Policy(kind=wcfg.FRAME_THRESHOLD, max_fresh_frame_dist=int(rng.integers(0, 3)))
+    else:
+        pol = Policy(kind=wcfg.CENTROID_THRESHOLD, max_fresh_centroid2=int(rng.integers(0, 2 * N)))
+    cfg = custom_config(name=f"split-sweep-{seed}", idx=300 + seed, heads=H, head_dim=D,
+                        frames=T, grid_h=gh_, grid_w=gw, num_partitions=P, steps=S,
+                        qkv_dtype="bf16", cache_dtype="bf16", schedule=wcfg.AnchorThen(pol))
+    return cfg, int(rng.integers(1, 4)), int(rng.integers(2, 5))
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_split_sweep(dita, monkeypatch, seed):
+    """Random workloads with forced splits, every element of every head and step against
+    the oracle; odd seeds hand Q, K, V and out over as [B, N, H, D].  A drawn workload whose
+    XCD ranges cannot all give K row groups (the library then splits none) is redrawn."""
+    from test_gpu_parity import active_for, run_and_check
+
+    def required(cfg, k, parts):
+        monkeypatch.setenv("DITA_SPLITS_PER_XCD", str(k))
+        monkeypatch.setenv("DITA_SPLIT_PARTS", str(parts))
+        return dita.dita_cache_required_bytes(dita.geometry_from(cfg), active_for(cfg))
+
+    for sub in range(20):
+        cfg, k, parts = _split_sweep_case(seed, sub)
+        if required(cfg, k, parts) - required(cfg, 0, parts) >= _split_bytes(cfg, 8 * k, parts):
+            break
+    else:
+        pytest.fail("no drawn workload splits")
+    required(cfg, k, parts)                        # leaves the variables set for the run
+    log(f"case {cfg.name} (draw {sub}): {8 * k} row groups split in {parts}")
+    run_and_check(dita, cfg, heads=[(0, h) for h in range(cfg.heads)],
+                  layout="bnhd" if seed % 2 else "bhnd")
