@@ -578,6 +578,9 @@ struct dita_cache {
   uint8_t* dev = nullptr;
   size_t dev_bytes = 0;
   std::vector<uint8_t> valid;        // P*P slot holds a state
+  // P*P: a merged member whose own state was dropped by a compaction (its state is its
+  // group's); not a fixed softmax reference until the block is computed again
+  std::vector<uint8_t> own_lost;
   std::vector<int32_t> last_fresh;   // P*P step at which the slot was written (0 = never)
   bool has_pending = false;
   Plan pending;
@@ -990,6 +993,7 @@ dita_status dita_cache_alloc(const dita_geometry* geom, const uint8_t* active_ma
   c->dev = (uint8_t*)device_buffer;
   c->dev_bytes = buffer_bytes;
   c->valid.assign((size_t)c->g.P * c->g.P, 0);
+  c->own_lost.assign((size_t)c->g.P * c->g.P, 0);
   c->last_fresh.assign((size_t)c->g.P * c->g.P, 0);
   c->fresh_step.assign((size_t)c->g.P * c->g.P, 0);
   c->w.assign((size_t)c->g.P * c->g.P, 0.f);
@@ -1101,7 +1105,12 @@ dita_status dita_set_block_policy(dita_cache* c, const dita_block_policy* policy
       if (covered[b] && M[b] == DITA_FRESH)
         return fail(DITA_ERR_POLICY, "block (%d,%d) is compacted with its group into one slot; "
                     "recomputing it needs dita_cache_expand first", (int)(b / P), (int)(b % P));
-  build_lists(c->g.P, M, covered.data(), c->valid.data(), &c->pending);
+  // a fresh block's cached lse is its fixed softmax reference only while its slot holds its
+  // own state
+  std::vector<uint8_t> prior(c->valid);
+  for (size_t b = 0; b < prior.size(); ++b)
+    if (c->own_lost[b]) prior[b] = 0;
+  build_lists(c->g.P, M, covered.data(), prior.data(), &c->pending);
   c->pending.planner_w = meas_w;
   c->pending.planner_delta = meas_delta;
   c->has_pending = true;
@@ -1292,6 +1301,7 @@ dita_status step_impl(dita_cache* c, const void* q, const void* k, const void* v
   for (size_t b = 0; b < PP; ++b)
     if (c->pending.mask[b] == DITA_FRESH) {
       c->valid[b] = 1;
+      c->own_lost[b] = 0;
       c->last_fresh[b] = (int32_t)c->steps_done;
       c->fresh_step[b] = c->steps_since_reset;
       c->head[b] = (int32_t)(b % c->g.P);      // recomputed: its own state again
@@ -1657,8 +1667,14 @@ dita_status dita_cache_compact(dita_cache* c, void* device_buffer, size_t buffer
   if (st) return st;
   std::vector<int32_t> slot_of, pairs;
   const int n = compact_slots(c, &slot_of, &pairs);
-  return rebind_slots(c, std::move(slot_of), n, pairs, device_buffer, buffer_bytes, hip_stream,
-                      true);
+  st = rebind_slots(c, std::move(slot_of), n, pairs, device_buffer, buffer_bytes, hip_stream,
+                    true);
+  if (st) return st;
+  // merged members now share their group's slot: their own states are gone
+  const int P = c->g.P;
+  for (size_t b = 0; b < c->head.size(); ++b)
+    if (c->head[b] != (int32_t)(b % P)) c->own_lost[b] = 1;
+  return ok();
 }
 
 dita_status dita_cache_expand(dita_cache* c, void* device_buffer, size_t buffer_bytes,
