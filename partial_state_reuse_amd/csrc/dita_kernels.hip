@@ -1061,16 +1061,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
 // Composizione dello Stato": partial attention states combine through their log-sum-exp in
 // any grouping; here as partial merges of the rows: part p's weighted by 2^(m_p - m), m the
 // largest, summed in the order of the parts, whichever finished first), then the rows written
-// as finish_rows does for a whole group.  One workgroup of 256 threads per split group;
-// thread t takes the values thread t of each part's workgroup left.  In the conditional
-// second pass it runs only if the first pass rejected a reference.
+// as finish_rows does for a whole group.  One wave per (split group, 32-row sub-tile):
+// workgroup 4 s + w takes the values wave w of each part's workgroup left, thread for
+// thread.  In the conditional second pass it runs only if the first pass rejected a
+// reference.
 template <int DP>
-__global__ __launch_bounds__(256) void merge_splits(StepArgs a) {
+__global__ __launch_bounds__(64) void merge_splits(StepArgs a) {
   constexpr int NDT = DP / 32;
   constexpr int W = 2 + NDT * 16;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int wave = blockIdx.x % kWaves, tid = wave * 64 + (int)threadIdx.x;
   if (a.fixup && a.counters[4] == 0) return;
-  const int s = blockIdx.x;
+  const int s = blockIdx.x / kWaves;
   const cint* plan = as_const(a.plan);
   const int bh = plan[a.off_splits + 2 * s], packed = plan[a.off_splits + 2 * s + 1];
   const int i = packed >> 16, t = packed & 0xffff;
@@ -1605,7 +1606,7 @@ hipError_t launch_step_bf16(const StepArgs& args, hipStream_t s) {
   const int m = a.delta_part != nullptr ? 1 : 0, f = a.cache_fp8 ? 2 : 0;
   const bool fixed = a.fixed_ref && (!m || a.diag_snap);
 #define DITA_MERGE_SPLITS(DPV)                                                                   \
-  if (a.num_splits > 0) hipLaunchKernelGGL((merge_splits<DPV>), dim3(a.num_splits), dim3(256), 0, s, a);
+  if (a.num_splits > 0) hipLaunchKernelGGL((merge_splits<DPV>), dim3(a.num_splits * kWaves), dim3(64), 0, s, a);
 #define DITA_LAUNCH_BF16(DPV)                                                                    \
   if (fixed) {                                                                                   \
     switch (m | f) {                                                                             \
