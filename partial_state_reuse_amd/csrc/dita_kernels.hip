@@ -849,10 +849,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   constexpr int CHV = DP * KT / 8 / 256;   // ... per V^T tile
   constexpr int WG_ROWS = kWaves * 32;
   // K tile, then V^T tile; the tail workgroups use the same memory for one slot of 2 + DP / 2
-  // floats per lane and wave (partial states and merges)
+  // floats per lane and wave (partial states and merges).  At DP >= 96 (2 waves per SIMD,
+  // 256 VGPRs) the row groups keep the d tiles dt >= AF of the row's running merge in LDS
+  // after the tiles between block ends (16 floats per lane and d tile), which frees their
+  // registers in the tile loop; at DP = 64 all of it stays in registers (AF = NDT).
   constexpr int TILE_ELEMS = KT * LDK + DP * LDV;
   constexpr int MERGE_ELEMS = kWaves * (2 + DP / 2) * 64 * 2;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[TILE_ELEMS > MERGE_ELEMS ? TILE_ELEMS : MERGE_ELEMS];
+  constexpr int AF = DP >= 96 ? 2 : NDT;
+  constexpr int ACC_ELEMS = kWaves * 64 * (NDT - AF) * 16 * 2;
+  constexpr int RG_ELEMS = TILE_ELEMS + ACC_ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[RG_ELEMS > MERGE_ELEMS ? RG_ELEMS : MERGE_ELEMS];
   uint16_t* const sK = smem;
   uint16_t* const sV = smem + KT * LDK;
 
@@ -912,11 +918,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     }
   }
 
-  // running merge of the row (base-2 units)
+  // running merge of the row (base-2 units); its d tiles dt >= AF in LDS between block ends,
+  // 4-float chunk q of d tile dt for lane l at ((dt - AF) * 4 + q) * 64 + l (the wave's own
+  // region: no barrier)
   f32x16 acc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x16){};
   float m_row = kNegInf, l_row = 0.f;
+  f32x4* const acc_lds = (f32x4*)(smem + TILE_ELEMS) +
+                         (size_t)__builtin_amdgcn_readfirstlane(wave) * (64 * (NDT - AF) * 4);
+  auto acc_put = [&](const f32x16 (&v)[NDT]) {
+#pragma unroll
+    for (int dt = AF; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc_lds[((dt - AF) * 4 + q) * 64 + lane] =
+            (f32x4){v[dt][4 * q], v[dt][4 * q + 1], v[dt][4 * q + 2], v[dt][4 * q + 3]};
+  };
+  auto acc_get = [&](f32x16 (&v)[NDT]) {
+#pragma unroll
+    for (int dt = AF; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 w = acc_lds[((dt - AF) * 4 + q) * 64 + lane];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[dt][4 * q + x] = w[x];
+      }
+  };
+  if (AF < NDT && live) acc_put(acc);
 
   const size_t slot_elems = (size_t)a.slot_rows * DP;
   typename CacheElem<FP8>::type* cache_o = (typename CacheElem<FP8>::type*)a.cache_o;
@@ -1036,11 +1065,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
         atomicOr(&a.counters[4], 1ull);
     }
 
+    if (AF < NDT) acc_get(acc);
     block_end<NDT, MEASURE, FP8>(a, bacc, m_b, l_b, paddr, (size_t)bh * a.num_slots + slot, row0, myrow,
                    cache_o + ((size_t)bh * a.num_slots + slot) * slot_elems + (size_t)row0 * DP,
                    acc, m_row, l_row, j == i, n_i, i, bh);
+    if (AF < NDT) acc_put(acc);
   }
   if (!live) return;
+  if (AF < NDT) acc_get(acc);
 
   reuse_fold<DP, FP8, 1>(a, bh, row0, e0, nf + r_lo, nf + r_hi, acc, m_row, l_row);
   if (split < 0) {
