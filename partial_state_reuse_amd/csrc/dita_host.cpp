@@ -261,6 +261,12 @@ dita_status resolve_geometry(const dita_geometry* g, Geo* out) {
   r.kt_pad = r.poffs[r.P];
   r.slot_rows = (int)align_up(max_n, dita::kSlotRowAlign);
   if (r.bf16()) {
+    // the step kernel's tile loads take 32-bit byte offsets inside a head's V^T and inside a
+    // tile of 64 key rows of K
+    const int64_t ld = r.layout == DITA_LAYOUT_BNHD ? (int64_t)r.H * r.D : r.D;
+    if ((int64_t)r.DP * r.kt_pad * 2 >= ((int64_t)1 << 31) ||
+        (int64_t)dita::kKeyTile * ld * 2 >= ((int64_t)1 << 31))
+      return fail(DITA_ERR_SHAPE, "a head's padded V^T or a tile of key rows exceeds 2 GiB");
     const int64_t G0 = (int64_t)r.B * r.H * r.num_tiles;
     if (G0 + dita::kMaxSplits >= ((int64_t)1 << 28))
       return fail(DITA_ERR_SHAPE, "too many workgroups (%lld)", (long long)G0);

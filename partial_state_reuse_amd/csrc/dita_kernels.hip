@@ -94,6 +94,17 @@ typedef __attribute__((address_space(4))) const int32_t cint;
 __device__ __forceinline__ const cint* as_const(const int32_t* p) { return (const cint*)p; }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+// A raw buffer resource over the bytes [base, base + bytes) (bytes above 2^32 - 1 clamped):
+// a load through it takes a wave-uniform base and a 32-bit per-lane byte offset (no 64-bit
+// address arithmetic), and a load at an offset past the end returns zeros.  Word 3 is the
+// raw-buffer setting of the gfx9 family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = (uint32_t)(bytes >> 32) != 0u ? 0xffffffffu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
@@ -952,6 +963,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   const uint16_t* Kg = (const uint16_t*)a.k + head_base(a, bh);
   const uint16_t* VTg = (const uint16_t*)a.vt + (size_t)bh * DP * a.kt_pad;
 
+  // the threads' byte offsets in a tile's loads, the same for every tile: K chunk m is key
+  // row c / (DP / 8) of the tile, dims d8 .. d8 + 7 (the last 8 dims of the head for the
+  // chunks past D); V^T chunk m is dim c / (KT / 8), keys k8 .. k8 + 7 (c = tid + 256 m)
+  const char* const k_end = (const char*)a.k + (size_t)a.B * a.sB * 2;
+  uint32_t kbyte[CHK], vbyte[CHV];
+#pragma unroll
+  for (int m = 0; m < CHK; ++m) {
+    const int c = tid + 256 * m;
+    kbyte[m] = ((uint32_t)(c / (DP / 8)) * (uint32_t)a.ld + (uint32_t)min((c % (DP / 8)) * 8, a.D - 8)) * 2u;
+  }
+#pragma unroll
+  for (int m = 0; m < CHV; ++m) {
+    const int c = tid + 256 * m;
+    vbyte[m] = ((uint32_t)(c / (KT / 8)) * (uint32_t)a.kt_pad + (uint32_t)(c % (KT / 8)) * 8u) * 2u;
+  }
+
   // ---------------- fresh blocks ----------------
   for (int e = f_lo; e < f_hi; ++e) {
     const int j = ent[2 * (e0 + e)], slot = ent[2 * (e0 + e) + 1];
@@ -968,21 +995,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
     float l_b = 0.f;                  // this lane's partial sum (16 of the 32 keys)
     float thr = kNegInf;              // rescale threshold: (m_b + slack) / (tau log2 e)
 
+    // a tile's loads: buffer loads from a resource based at the tile's first key (K: its row,
+    // V^T: its column; wave-uniform) at the thread's fixed byte offset.  K rows past the block
+    // are read as they stand (the next partition's) or, past the end of K, as zeros, and their
+    // scores are masked.
     u32x4 pk[CHK], pv[CHV];
     auto fetch = [&](int kt) {
+      const char* Kt = (const char*)(Kg + (size_t)(o_j + kt * KT) * a.ld);
+      const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(Kt, (uint64_t)(k_end - Kt));
+      const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(VTg + po_j + kt * KT, ~0ull);
 #pragma unroll
-      for (int m = 0; m < CHK; ++m) {
-        const int c = tid + 256 * m;
-        const int r = c / (DP / 8), d8 = (c % (DP / 8)) * 8;
-        const int key = min(kt * KT + r, n_j - 1);
-        pk[m] = ld16(Kg + (size_t)(o_j + key) * a.ld + min(d8, a.D - 8));
-      }
+      for (int m = 0; m < CHK; ++m) pk[m] = buf16(rk, kbyte[m]);
 #pragma unroll
-      for (int m = 0; m < CHV; ++m) {
-        const int c = tid + 256 * m;
-        const int d = c / (KT / 8), k8 = (c % (KT / 8)) * 8;
-        pv[m] = ld16(VTg + (size_t)d * a.kt_pad + po_j + kt * KT + k8);
-      }
+      for (int m = 0; m < CHV; ++m) pv[m] = buf16(rv, vbyte[m]);
     };
     fetch(0);
     for (int kt = 0; kt < ntile; ++kt) {
