@@ -859,6 +859,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
   constexpr int CHK = KT * DP / 8 / 256;   // 16-byte chunks per thread per K tile
   constexpr int CHV = DP * KT / 8 / 256;   // ... per V^T tile
   constexpr int WG_ROWS = kWaves * 32;
+  constexpr bool AHEAD = DP == 64;    // LDS fragment reads issued ahead of their MFMAs
   // K tile, then V^T tile; the tail workgroups use the same memory for one slot of 2 + DP / 2
   // floats per lane and wave (partial states and merges).  At DP >= 96 (2 waves per SIMD,
   // 256 VGPRs) the row groups keep the d tiles dt >= AF of the row's running merge in LDS
@@ -1026,17 +1027,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
       if (kt + 1 < ntile) fetch(kt + 1);
       if (!live) continue;
 
+      // fragment reads from LDS: with AHEAD (DP = 64, where the registers allow it) the next
+      // half's K fragments are read as soon as this half's QK MFMAs are issued, and this
+      // half's V^T fragments before its softmax, so that the MFMAs seldom wait for the LDS;
+      // otherwise each fragment is read where it is used
+      auto k_frag = [&](int ks, int kc) {
+        return as_bf16x8(ld16(&sK[(ks * 32 + key_of_row(l32)) * LDK + kc * 16 + h32 * 8]));
+      };
+      auto v_frag = [&](int ks, int dt, int c) {
+        return as_f16x8(ld16(&sV[(dt * 32 + l32) * LDV + ks * 32 + c * 16 + h32 * 8]));
+      };
+      bf16x8 kcur[NKC], knext[NKC];
+      if constexpr (AHEAD) {
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) kcur[kc] = k_frag(0, kc);
+      }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int kbase = kt * KT + ks * 32;   // first key of this half (partition-relative)
         if (kbase >= n_j) break;
         // S^T = K Q^T over this 32-key half
         f32x16 s = (f32x16){};
-        const int krow = ks * 32 + key_of_row(l32);
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const bf16x8 kf = as_bf16x8(ld16(&sK[krow * LDK + kc * 16 + h32 * 8]));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s, 0, 0, 0);
+        for (int kc = 0; kc < NKC; ++kc)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AHEAD ? kcur[kc] : k_frag(ks, kc), qf[kc],
+                                                      s, 0, 0, 0);
+        f16x8 vfr[NDT][2];
+        if constexpr (AHEAD) {
+          if (ks + 1 < NKS) {
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) knext[kc] = k_frag(ks + 1, kc);
+          }
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) vfr[dt][c] = v_frag(ks, dt, c);
         }
         if (kbase + 32 > n_j) {
 #pragma unroll
@@ -1076,11 +1101,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DP == 64 ? 
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const f16x8 vf = as_f16x8(
-                ld16(&sV[(dt * 32 + l32) * LDV + ks * 32 + c * 16 + h32 * 8]));
-            bacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], bacc[dt], 0, 0, 0);
-          }
+          for (int c = 0; c < 2; ++c)
+            bacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AHEAD ? vfr[dt][c] : v_frag(ks, dt, c),
+                                                              pf[c], bacc[dt], 0, 0, 0);
+        if constexpr (AHEAD) {
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) kcur[kc] = knext[kc];
+        }
       }
     }
     if (!live) continue;
