@@ -372,6 +372,15 @@ def test_full_video29f_720p(dita):
     _full(dita, 3, heads=[(0, 0), (0, 13), (0, 23)], per_part=12)
 
 
+def test_full_video29f_720p_every_row_of_one_head(dita):
+    """The 29-frame workload at full size in the bench's launch configuration, every row and
+    every element of one head over the whole 10-step schedule (the anchor's running-maximum
+    kernel, then nine fixed-reference passes with 608 of 1024 states reused), against the fp64
+    oracle: the row groups, the packed tail sub-tiles (4 rows of every partition) and the
+    split row groups all write rows of this head."""
+    run_and_check(dita, CONFIGS[3], heads=[(0, 11)], rows=None, recomputes=0)
+
+
 def test_full_video29f_720p_token_major(dita):
     """The same workload with Q, K, V and out as [B, N, H, D] (a token stride of H D = 1536)."""
     _full(dita, 3, heads=[(0, 5), (0, 18)], per_part=8, layout="bnhd")
