@@ -381,6 +381,13 @@ def test_full_video29f_720p_every_row_of_one_head(dita):
     run_and_check(dita, CONFIGS[3], heads=[(0, 11)], rows=None, recomputes=0)
 
 
+def test_full_video93f_every_row_of_one_head(dita):
+    """The 93-frame tile-sparse workload at full size (86400 tokens, 24 partitions of 3600,
+    92 of 576 blocks active), every element of one head over its anchor and first reuse step,
+    against the fp64 oracle."""
+    run_and_check(dita, CONFIGS[4], heads=[(0, 7)], rows=None, steps=2, recomputes=0)
+
+
 def test_full_video29f_720p_token_major(dita):
     """The same workload with Q, K, V and out as [B, N, H, D] (a token stride of H D = 1536)."""
     _full(dita, 3, heads=[(0, 5), (0, 18)], per_part=8, layout="bnhd")
