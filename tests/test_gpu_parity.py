@@ -388,6 +388,14 @@ def test_full_video93f_every_row_of_one_head(dita):
     run_and_check(dita, CONFIGS[4], heads=[(0, 7)], rows=None, steps=2, recomputes=0)
 
 
+def test_full_cfg_long_video_every_row_of_one_head(dita):
+    """The CFG workload at full size (B = 2, 40 heads, 26520 tokens, D = 128, 16 partitions of
+    1658/1657), every element of one head of the second branch over its two anchor steps (the
+    running-maximum kernel, then the fixed-reference pass with every block fresh) and its first
+    step with 70 % of the states reused, against the fp64 oracle."""
+    run_and_check(dita, CONFIGS[5], heads=[(1, 39)], rows=None, steps=3, recomputes=0)
+
+
 def test_full_video29f_720p_token_major(dita):
     """The same workload with Q, K, V and out as [B, N, H, D] (a token stride of H D = 1536)."""
     _full(dita, 3, heads=[(0, 5), (0, 18)], per_part=8, layout="bnhd")
