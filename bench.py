@@ -393,11 +393,13 @@ def main():
                 spare[0] = old
             cache.reset()
         cache.set_policy(policies[s])
-        pl = cache.plan()                             # host copy of the plan, no device wait
-        step_masks.append((pl["mask"], pl["reuse_ptr"]))
         q, kk, v = dev[s]
         cache.step(q, kk, v, out=out, lse=lse, stream=stream,
                    static_scratch=args.static_scratch)
+        # host copy of the step's plan (no device wait), taken after the launch so that it
+        # adds nothing between a planner step's decision and its kernels
+        pl = cache.plan()
+        step_masks.append((pl["mask"], pl["reuse_ptr"]))
         if s == 0:
             for g, sel in merge_sel:
                 cache.merge_groups(g, select=sel, stream=stream)
